@@ -1,0 +1,245 @@
+"""Benchmark of the packed low-bit KV decode step on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME]
+
+One step = kvq_decode_attention + kvq_combine over the whole cache of the workload (the
+decode-attention step the metric names). Inputs are resident in HBM before timing starts.
+To keep the 256 MB Infinity Cache (MALL) from serving the reads, the timed loop rotates
+over enough independent copies of the packed cache to exceed 512 MB. Also measured, and
+reported next to the step: the flush (kvq_quantize_pack of the 128-token window of every
+row), the one-token append, a plain device copy as a bandwidth reference, and the CPU
+oracle on a bounded sample of the same workload.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "decode-attn µs/step + effective KV GB/s (% HBM peak), L=32K 4-bit GQA"
+HBM_PEAK_GBPS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama8b_32k")
+    ap.add_argument("--splits", type=int, default=0, help="0 = the library's suggestion")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def kernel_source_digest() -> str:
+    h = hashlib.sha256()
+    for f in ("decode_attn.hip", "kvq_device.h"):
+        with open(os.path.join(ROOT, "bit_kv_cache_pack_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary, if it was
+    taken on the current decode kernel source."""
+    p = os.path.join(ROOT, "profiles", f"decode_{workload}_traffic.md")
+    if not os.path.exists(p):
+        return None
+    txt = open(p).read()
+    m = re.search(r"kernel_source_digest:\s*(\w+)", txt)
+    t = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", txt)
+    if not m or not t or m.group(1) != kernel_source_digest():
+        return None
+    return float(t.group(1))
+
+
+def cpu_baseline(wl, x, seconds: float):
+    """The CPU oracle (fp64 dequant + attention), as it stands, on the host cores."""
+    import numpy as np
+    from oracle import oracle as O
+    rows = wl.B * wl.Hkv
+    fmt = O.Format(wl.bits, 128, wl.hybrid)
+    kps, vps = x.packed_src()
+    kp = O.quantize_pack(fmt, np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128)))
+    vp = O.quantize_pack(fmt, np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128)))
+    kr, vr = x.residual()
+    threads = O.default_threads()
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        O.attention(fmt, x.q, wl.Hkv, kp, vp, wl.n_packed, kr, vr, wl.n_res, n_threads=threads)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    step_s = el / reps
+    return {"value": round(wl.step_bytes() / step_s / 1e9, 4), "unit": "GB/s",
+            "cores": threads, "kind": "oracle",
+            "ms_per_step": round(step_s * 1e3, 3),
+            "sample": f"{reps} full decode steps of {wl.name} (all {wl.B * wl.Hq} heads, "
+                      f"{wl.L} tokens; dequantize + fp64 softmax attention), {el:.1f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); this build has no "
+              "multi-GPU path. Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import synth_inputs as S
+    from bit_kv_cache_pack_amd import kvq as K
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = S.WORKLOADS[args.workload]
+    fmt = K.Format(wl.bits, 128, wl.hybrid)
+    rows = wl.B * wl.Hkv
+    bb = fmt.block_bytes
+    nb = wl.n_packed // 128
+    S_ = args.splits or K.suggest_splits(wl.B, wl.Hkv, wl.L,
+                                         torch.cuda.get_device_properties(dev).multi_processor_count)
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+
+    x = S.make_inputs(wl)
+    kps, vps = x.packed_src()
+    kr, vr = x.residual()
+    kps_d = torch.from_numpy(np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128))).to(dev)
+    vps_d = torch.from_numpy(np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128))).to(dev)
+    kp0 = torch.empty((rows, nb * bb), dtype=torch.uint8, device=dev)
+    vp0 = torch.empty_like(kp0)
+    K.kvq_quantize_pack(fmt, kps_d, rows, wl.n_packed, wl.n_packed * 128, 128, kp0, nb * bb, 0)
+    K.kvq_quantize_pack(fmt, vps_d, rows, wl.n_packed, wl.n_packed * 128, 128, vp0, nb * bb, 0)
+    del kps_d, vps_d
+    step_bytes = wl.step_bytes()
+    copies = max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+    kr_d = torch.from_numpy(kr).to(dev)
+    vr_d = torch.from_numpy(vr).to(dev)
+    caches = [(kp0, vp0, kr_d, vr_d)] + [(kp0.clone(), vp0.clone(), kr_d.clone(), vr_d.clone())
+                                         for _ in range(copies - 1)]
+    q = torch.from_numpy(x.q).to(dev)
+    part_o = torch.empty((wl.B, wl.Hq, S_, 128), dtype=torch.float32, device=dev)
+    part_lse = torch.empty((wl.B, wl.Hq, S_), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sptr = stream.cuda_stream
+
+    def step(i, ev=None):
+        kp, vp, krd, vrd = caches[i % copies]
+        if ev is not None:
+            ev[0].record(stream)
+        K.kvq_decode_attention(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed, krd, vrd,
+                               128, wl.n_res, sm, S_, part_o, part_lse, stream=sptr)
+        if ev is not None:
+            ev[1].record(stream)
+        K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sptr)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, evs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    # flush (quantize the full 128-token window of every row, K and V) and append
+    fl_reps = 50
+    fsrc = [(c[2], c[3]) for c in caches]
+    fdst = torch.empty((rows, bb), dtype=torch.uint8, device=dev)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for i in range(fl_reps + 5):
+        if i == 5:
+            e0.record(stream)
+        kr_, vr_ = fsrc[i % copies]
+        K.kvq_quantize_pack(fmt, kr_, rows, 128, 128 * 128, 128, fdst, bb, 0, stream=sptr)
+        K.kvq_quantize_pack(fmt, vr_, rows, 128, 128 * 128, 128, fdst, bb, 0, stream=sptr)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    flush_ms = e0.elapsed_time(e1) / fl_reps
+    kn = torch.zeros((wl.B, wl.Hkv, 128), dtype=torch.float16, device=dev)
+    scratch_res = [torch.empty_like(kr_d), torch.empty_like(vr_d)]
+    for i in range(fl_reps + 5):
+        if i == 5:
+            e0.record(stream)
+        K.kvq_append_residual(kn, kn, scratch_res[0], scratch_res[1], wl.B, wl.Hkv, 128, 128,
+                              i % 128, stream=sptr)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    append_ms = e0.elapsed_time(e1) / fl_reps
+
+    # plain device copy as a bandwidth reference (read + write bytes)
+    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    for _ in range(3):
+        big2.copy_(big)
+    e0.record(stream)
+    for _ in range(10):
+        big2.copy_(big)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * big.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del big, big2
+
+    achieved = step_bytes / (dec_ms * 1e-3) / 1e9
+    traffic = recorded_traffic(wl.name)
+    result = {
+        "metric": METRIC,
+        "value": round(step_bytes / (ms_per_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_step": round(ms_per_step * 1e3, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
+        "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "flush_us": round(flush_ms * 1e3, 3),
+        "append_us": round(append_ms * 1e3, 3),
+        "step_us_with_append_and_amortized_flush": round((ms_per_step + append_ms + flush_ms / 128)
+                                                         * 1e3, 3),
+        "copy_reference_gbps": round(copy_gbps, 1),
+        "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L,
+                   "bits": wl.bits, "group": 32, "hybrid": wl.hybrid, "n_packed": wl.n_packed,
+                   "n_res": wl.n_res, "splits": S_, "cache_copies": copies,
+                   "algorithmic_bytes_per_step": step_bytes},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "kernel": "decode_kernel (kvq_decode_attention)"},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,139 @@
+// kvq_api.cpp -- the extern "C" boundary of libkvq: argument validation, then launches.
+// Every check runs on the host before anything is enqueued; see include/kvq.h for the
+// contract of each call.
+#include "kvq.h"
+
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+bool aligned64(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 63u) == 0; }
+
+kvq_status check_format(const kvq_format *f)
+{
+    if (!f) return KVQ_ERR_NULL;
+    if (f->bits < 2 || f->bits > 4 || f->group != 32 || f->block_tokens != 128 ||
+        (f->hybrid != 0 && f->hybrid != 1))
+        return KVQ_ERR_UNSUPPORTED;
+    if (f->head_dim <= 0 || f->head_dim % 32 != 0) return KVQ_ERR_SHAPE;
+    if (f->head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+    return KVQ_OK;
+}
+
+kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                             int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                             void *dst_packed, int64_t dst_row_stride_bytes,
+                             int32_t dst_first_block, hipStream_t stream)
+{
+    kvq_status st = check_format(fmt);
+    if (st != KVQ_OK) return st;
+    if (!src_fp16 || !dst_packed) return KVQ_ERR_NULL;
+    if (n_rows < 1 || n_tokens < 128 || n_tokens % 128 != 0 || dst_first_block < 0)
+        return KVQ_ERR_SHAPE;
+    if (src_tok_stride < fmt->head_dim || src_row_stride < 0) return KVQ_ERR_SHAPE;
+    if (src_row_stride % 8 != 0 || src_tok_stride % 8 != 0) return KVQ_ERR_ALIGN;
+    if (!aligned64(src_fp16) || !aligned64(dst_packed) || dst_row_stride_bytes % 64 != 0)
+        return KVQ_ERR_ALIGN;
+    const int64_t bb = kvq_block_bytes(fmt);
+    const int64_t nb = n_tokens / 128;
+    if (dst_row_stride_bytes < ((int64_t)dst_first_block + nb) * bb) return KVQ_ERR_SHAPE;
+    if (n_rows * nb > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    return launched(kvq::launch_quantize_pack(
+        fmt->bits, fmt->hybrid, static_cast<const uint16_t *>(src_fp16), n_rows, n_tokens,
+        src_row_stride, src_tok_stride, static_cast<uint8_t *>(dst_packed), dst_row_stride_bytes,
+        dst_first_block, (int32_t)bb, (int32_t)kvq_sz_offset(fmt), (int32_t)kvq_flag_offset(fmt),
+        stream));
+}
+
+kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                int32_t Hq, int32_t Hkv, const void *k_packed,
+                                const void *v_packed, int64_t packed_row_stride_bytes,
+                                int32_t n_packed_tokens, const void *k_res_fp16,
+                                const void *v_res_fp16, int32_t res_capacity, int32_t n_res,
+                                float sm_scale, int32_t num_splits, float *part_o,
+                                float *part_lse, hipStream_t stream)
+{
+    kvq_status st = check_format(fmt);
+    if (st != KVQ_OK) return st;
+    if (!q_fp16 || !part_o || !part_lse) return KVQ_ERR_NULL;
+    if (n_packed_tokens > 0 && (!k_packed || !v_packed)) return KVQ_ERR_NULL;
+    if (n_res > 0 && (!k_res_fp16 || !v_res_fp16)) return KVQ_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return KVQ_ERR_SHAPE;
+    if (n_packed_tokens < 0 || n_packed_tokens % 128 != 0) return KVQ_ERR_SHAPE;
+    if (n_res < 0 || res_capacity < 0 || n_res > res_capacity) return KVQ_ERR_SHAPE;
+    if ((int64_t)n_packed_tokens + n_res <= 0) return KVQ_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
+    if (!isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+    if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
+    const int64_t bb = kvq_block_bytes(fmt);
+    if (n_packed_tokens > 0) {
+        if (packed_row_stride_bytes % 64 != 0) return KVQ_ERR_ALIGN;
+        if (packed_row_stride_bytes < (int64_t)(n_packed_tokens / 128) * bb) return KVQ_ERR_SHAPE;
+        if (!aligned64(k_packed) || !aligned64(v_packed)) return KVQ_ERR_ALIGN;
+    }
+    if (n_res > 0 && (!aligned64(k_res_fp16) || !aligned64(v_res_fp16))) return KVQ_ERR_ALIGN;
+    if (!aligned64(q_fp16) || !aligned64(part_o) || !aligned64(part_lse)) return KVQ_ERR_ALIGN;
+    kvq::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q_fp16);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.kp = static_cast<const uint8_t *>(k_packed);
+    p.vp = static_cast<const uint8_t *>(v_packed);
+    p.row_stride = packed_row_stride_bytes;
+    p.n_packed = n_packed_tokens;
+    p.kres = static_cast<const uint16_t *>(k_res_fp16);
+    p.vres = static_cast<const uint16_t *>(v_res_fp16);
+    p.res_cap = res_capacity;
+    p.n_res = n_res;
+    p.sm_scale = sm_scale;
+    p.num_splits = num_splits;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    p.bits = fmt->bits;
+    p.block_bytes = (int32_t)bb;
+    p.sz_off = (int32_t)kvq_sz_offset(fmt);
+    return launched(kvq::launch_decode(p, stream));
+}
+
+kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
+                       int32_t head_dim, int32_t num_splits, void *out, int32_t out_dtype,
+                       hipStream_t stream)
+{
+    if (!part_o || !part_lse || !out) return KVQ_ERR_NULL;
+    if (B < 1 || Hq < 1 || num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
+    if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+    if (out_dtype != KVQ_OUT_F32 && out_dtype != KVQ_OUT_F16) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (!aligned64(part_o) || !aligned64(part_lse) || !aligned64(out)) return KVQ_ERR_ALIGN;
+    return launched(kvq::launch_combine(part_o, part_lse, B, Hq, num_splits, out,
+                                        out_dtype == KVQ_OUT_F16, stream));
+}
+
+kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res, void *v_res,
+                               int32_t B, int32_t Hkv, int32_t head_dim, int32_t res_capacity,
+                               int32_t slot, hipStream_t stream)
+{
+    if (!k_new || !v_new || !k_res || !v_res) return KVQ_ERR_NULL;
+    if (B < 1 || Hkv < 1 || res_capacity < 1 || slot < 0 || slot >= res_capacity)
+        return KVQ_ERR_SHAPE;
+    if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (!aligned64(k_new) || !aligned64(v_new) || !aligned64(k_res) || !aligned64(v_res))
+        return KVQ_ERR_ALIGN;
+    return launched(kvq::launch_append(
+        static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
+        static_cast<uint16_t *>(k_res), static_cast<uint16_t *>(v_res), B, Hkv, res_capacity,
+        slot, stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,224 @@
+// quant_pack.hip -- group-wise low-bit quantization of fp16 K/V tokens into packed blocks.
+//
+// Follows the BitDecoding page ("Tensor Core加速的低比特KV缓存解码系统") sec. 2.1 for
+// scale = (max - min) / (2^b - 1) and code = round((x - min) / scale), and sec. 3.1 for the
+// register-only kernel shape (per-thread min/max, a cross-lane reduction, packing in
+// registers); the 3-bit blog page ("3-bit KV缓存量化：大模型推理功耗与带宽优化核心技术")
+// sec. 2.3 for the clip to [0, 2^b - 1] and sec. 3.2 for fp16 K/V -> packed codes +
+// scale/zero; the InnerQ page ("KV缓存量化技术InnerQ：提升大模型推理效率") sec. 2.1 for
+// groups of 32 along head_dim and sec. 2.2 for the per-group symmetric/asymmetric choice.
+//
+// Work mapping: one workgroup (4 waves) per (row, 128-token block). A lane owns 8
+// channels (one 16-byte load); 4 lanes (a DPP quad) hold one 32-channel group, 16 lanes
+// one token, so a wave covers 4 tokens per step and 32 tokens in all. The group min/max
+// and the hybrid error sums are quad reductions with DPP; a lane's 8 codes are exactly
+// `bits` bytes of the group's word, so every lane stores its own bytes.
+//
+// Every quantizer step is one IEEE binary32 operation (no contraction: see the pragma;
+// division is the correctly rounded one) so the bytes equal the CPU definition's.
+#include "kvq_device.h"
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+namespace {
+
+template <int CTRL>
+__device__ __forceinline__ float quad_dpp(float v) { return dpp_f<CTRL>(v); }
+
+__device__ __forceinline__ float round_half_away_pos(float t)
+{
+    const float k = __builtin_truncf(t);
+    return (t - k >= 0.5f) ? k + 1.0f : k;
+}
+__device__ __forceinline__ float round_half_away(float t)
+{
+    const float r = round_half_away_pos(__builtin_fabsf(t));
+    return t < 0.0f ? -r : r;
+}
+
+struct QPArgs {
+    const uint16_t *src;
+    int64_t src_row_stride, src_tok_stride;  // elements
+    uint8_t *dst;
+    int64_t dst_row_stride;                  // bytes
+    int32_t first_block, n_blocks;
+    int32_t block_bytes, sz_off, flag_off;
+};
+
+template <int BITS, bool HYBRID>
+__global__ __launch_bounds__(256) void quant_pack_kernel(QPArgs a)
+{
+    constexpr int N = (1 << BITS) - 1;
+    constexpr int OFF = 1 << (BITS - 1);
+    constexpr int QS = OFF - 1;
+    constexpr int GBYTES = 4 * BITS;   // bytes per packed group
+
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    const int64_t row = blockIdx.x / a.n_blocks;
+    const int blk = blockIdx.x % a.n_blocks;
+    const int tl = lane >> 4;          // token within a 4-token step
+    const int oct = lane & 15;         // channel octet 0..15
+    const int g = oct >> 2;            // group 0..3
+    const int j = oct & 3;             // octet within the group
+
+    __shared__ uint32_t flags[16];
+    if (HYBRID) {
+        if (threadIdx.x < 16) flags[threadIdx.x] = 0;
+        __syncthreads();
+    }
+
+    const uint16_t *src = a.src + row * a.src_row_stride + (int64_t)blk * kBlockTokens * a.src_tok_stride;
+    uint8_t *dblk = a.dst + row * a.dst_row_stride + (int64_t)(a.first_block + blk) * a.block_bytes;
+
+    // issue all 8 loads of this wave's 32 tokens first
+    u32x4 raw[8];
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int tb = wave * 32 + it * 4 + tl;
+        raw[it] = *reinterpret_cast<const u32x4 *>(src + (int64_t)tb * a.src_tok_stride + oct * 8);
+    }
+
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int tb = wave * 32 + it * 4 + tl;
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const half2_t h = as_h2(raw[it][i]);
+            x[2 * i] = (float)h.x;
+            x[2 * i + 1] = (float)h.y;
+        }
+        float mn = x[0], mx = x[0];
+#pragma unroll
+        for (int i = 1; i < 8; ++i) {
+            mn = fminf(mn, x[i]);
+            mx = fmaxf(mx, x[i]);
+        }
+        mn = fminf(mn, quad_dpp<0xB1>(mn));
+        mn = fminf(mn, quad_dpp<0x4E>(mn));
+        mx = fmaxf(mx, quad_dpp<0xB1>(mx));
+        mx = fmaxf(mx, quad_dpp<0x4E>(mx));
+        mn = mn + 0.0f;   // -0.0 -> +0.0
+        mx = mx + 0.0f;
+
+        // asymmetric candidate
+        const _Float16 sh = (_Float16)((mx - mn) / (float)N);
+        const _Float16 zh = (_Float16)mn;     // exact
+        const float s = (float)sh, z = (float)zh;
+        int code[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float c = 0.0f;
+            if (s != 0.0f) c = fminf(round_half_away_pos((x[i] - z) / s), (float)N);
+            code[i] = (int)c;
+        }
+        uint16_t out_s = __builtin_bit_cast(uint16_t, sh);
+        uint16_t out_z = __builtin_bit_cast(uint16_t, zh);
+        int flag = 1;
+
+        if (HYBRID) {
+            // symmetric candidate: signed grid k*ss, |k| <= QS, offset-binary codes
+            float am = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(x[i]));
+            am = fmaxf(am, quad_dpp<0xB1>(am));
+            am = fmaxf(am, quad_dpp<0x4E>(am));
+            const _Float16 ssh = (_Float16)(am / (float)QS);
+            const float ss = (float)ssh;
+            const float zs = -((float)OFF * ss) + 0.0f;
+            const bool eligible = __builtin_fabsf(zs) <= 65504.0f;
+            int scode[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float k = 0.0f;
+                if (ss != 0.0f) k = fminf(fmaxf(round_half_away(x[i] / ss), -(float)QS), (float)QS);
+                scode[i] = OFF + (int)k;
+            }
+            // squared errors, balanced pairwise sum in channel order: 8 in-lane, then quad
+            float ea[8], es[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float da = x[i] - __builtin_fmaf((float)code[i], s, z);
+                const float ds = x[i] - __builtin_fmaf((float)scode[i], ss, zs);
+                ea[i] = da * da;
+                es[i] = ds * ds;
+            }
+            float sa = ((ea[0] + ea[1]) + (ea[2] + ea[3])) + ((ea[4] + ea[5]) + (ea[6] + ea[7]));
+            float se = ((es[0] + es[1]) + (es[2] + es[3])) + ((es[4] + es[5]) + (es[6] + es[7]));
+            sa = sa + quad_dpp<0xB1>(sa);
+            sa = sa + quad_dpp<0x4E>(sa);
+            se = se + quad_dpp<0xB1>(se);
+            se = se + quad_dpp<0x4E>(se);
+            if (eligible && se < sa) {
+                flag = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) code[i] = scode[i];
+                out_s = __builtin_bit_cast(uint16_t, ssh);
+                out_z = __builtin_bit_cast(uint16_t, (_Float16)zs);
+            }
+        }
+
+        uint32_t packed = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) packed |= (uint32_t)code[i] << (BITS * i);
+
+        uint8_t *gptr = dblk + (tb * kGroups + g) * GBYTES + j * BITS;
+        if (BITS == 4) {
+            *reinterpret_cast<uint32_t *>(gptr) = packed;
+        } else if (BITS == 2) {
+            *reinterpret_cast<uint16_t *>(gptr) = (uint16_t)packed;
+        } else {
+            gptr[0] = (uint8_t)packed;
+            gptr[1] = (uint8_t)(packed >> 8);
+            gptr[2] = (uint8_t)(packed >> 16);
+        }
+        if (j == 0) {
+            *reinterpret_cast<uint32_t *>(dblk + a.sz_off + (tb * kGroups + g) * 4) =
+                (uint32_t)out_s | ((uint32_t)out_z << 16);
+            if (HYBRID && flag) {
+                const int bit = tb * kGroups + g;
+                atomicOr(&flags[bit >> 5], 1u << (bit & 31));
+            }
+        }
+    }
+    if (HYBRID) {
+        __syncthreads();
+        if (threadIdx.x < 16)
+            reinterpret_cast<uint32_t *>(dblk + a.flag_off)[threadIdx.x] = flags[threadIdx.x];
+    }
+}
+
+template <int BITS, bool HYBRID>
+hipError_t launch_t(const QPArgs &a, int64_t n_rows, hipStream_t stream)
+{
+    const int64_t n_wg = n_rows * a.n_blocks;
+    hipLaunchKernelGGL((quant_pack_kernel<BITS, HYBRID>), dim3((uint32_t)n_wg), dim3(256), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quantize_pack(int bits, int hybrid, const uint16_t *src, int64_t n_rows,
+                                int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                                uint8_t *dst, int64_t dst_row_stride, int32_t first_block,
+                                int32_t block_bytes, int32_t sz_off, int32_t flag_off,
+                                hipStream_t stream)
+{
+    QPArgs a{src, src_row_stride, src_tok_stride, dst, dst_row_stride, first_block,
+             n_tokens / kBlockTokens, block_bytes, sz_off, flag_off};
+    switch (bits * 2 + (hybrid ? 1 : 0)) {
+    case 4: return launch_t<2, false>(a, n_rows, stream);
+    case 5: return launch_t<2, true>(a, n_rows, stream);
+    case 6: return launch_t<3, false>(a, n_rows, stream);
+    case 7: return launch_t<3, true>(a, n_rows, stream);
+    case 8: return launch_t<4, false>(a, n_rows, stream);
+    case 9: return launch_t<4, true>(a, n_rows, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace kvq

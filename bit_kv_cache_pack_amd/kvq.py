@@ -1,0 +1,169 @@
+"""ctypes binding of libkvq (include/kvq.h): argument marshalling only.
+
+Each function has the name and the arguments of the C call. Tensors are passed as device
+pointers (torch is used for device memory and streams); `stream=None` means torch's
+current stream on the tensors' device. A non-zero status raises KVQError. Every step of
+the computation runs in the HIP kernels of libkvq.so; nothing here computes.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from dataclasses import dataclass
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkvq.so")
+
+KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_LAUNCH = \
+    0, -1, -2, -3, -4, -5
+KVQ_OUT_F32, KVQ_OUT_F16 = 0, 1
+_STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
+           -3: "unsupported format or shape", -4: "misaligned pointer or stride",
+           -5: "kernel launch failed"}
+
+EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_combine", "kvq_append_residual")
+
+
+class KVQError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {_STATUS.get(status, 'unknown status')} ({status})")
+        self.status = status
+
+
+class kvq_format(C.Structure):
+    _fields_ = [("bits", C.c_int32), ("head_dim", C.c_int32), ("group", C.c_int32),
+                ("hybrid", C.c_int32), ("block_tokens", C.c_int32)]
+
+
+@dataclass(frozen=True)
+class Format:
+    """Python view of kvq_format with the header's size helpers."""
+    bits: int
+    head_dim: int = 128
+    hybrid: bool = False
+    group: int = 32
+    block_tokens: int = 128
+
+    def c(self) -> kvq_format:
+        return kvq_format(self.bits, self.head_dim, self.group, int(self.hybrid),
+                          self.block_tokens)
+
+    @staticmethod
+    def _a64(v: int) -> int:
+        return (v + 63) // 64 * 64
+
+    @property
+    def codes_bytes(self) -> int:
+        return self.block_tokens * self.head_dim * self.bits // 8
+
+    @property
+    def sz_offset(self) -> int:
+        return self._a64(self.codes_bytes)
+
+    @property
+    def sz_bytes(self) -> int:
+        return self.block_tokens * (self.head_dim // self.group) * 4
+
+    @property
+    def flag_offset(self) -> int:
+        return self._a64(self.sz_offset + self.sz_bytes)
+
+    @property
+    def flag_bytes(self) -> int:
+        return (self.block_tokens * (self.head_dim // self.group) + 7) // 8 if self.hybrid else 0
+
+    @property
+    def block_bytes(self) -> int:
+        return self._a64(self.flag_offset + self.flag_bytes)
+
+
+_lib = None
+
+
+def lib():
+    """Load libkvq.so; raise if it has not been built (there is no fallback path)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m bit_kv_cache_pack_amd.build`")
+        L = C.CDLL(LIB_PATH)
+        vp, i32, i64, f32 = C.c_void_p, C.c_int32, C.c_int64, C.c_float
+        fp = C.POINTER(kvq_format)
+        L.kvq_quantize_pack.argtypes = [fp, vp, i64, i32, i64, i64, vp, i64, i32, vp]
+        L.kvq_decode_attention.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32,
+                                           i32, f32, i32, vp, vp, vp]
+        L.kvq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp]
+        L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        for n in EXPORTED:
+            getattr(L, n).restype = C.c_int
+        _lib = L
+    return _lib
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    import torch
+    dev = next((t.device for t in tensors if hasattr(t, "device") and t.device.type == "cuda"),
+               None)
+    return torch.cuda.current_stream(dev).cuda_stream
+
+
+def _check(fn: str, st: int):
+    if st != KVQ_OK:
+        raise KVQError(fn, st)
+
+
+def kvq_quantize_pack(fmt: Format, src_fp16, n_rows: int, n_tokens: int, src_row_stride: int,
+                      src_tok_stride: int, dst_packed, dst_row_stride_bytes: int,
+                      dst_first_block: int, stream=None):
+    f = fmt.c()
+    st = lib().kvq_quantize_pack(C.byref(f), _ptr(src_fp16), n_rows, n_tokens, src_row_stride,
+                                 src_tok_stride, _ptr(dst_packed), dst_row_stride_bytes,
+                                 dst_first_block, _stream(stream, src_fp16, dst_packed))
+    _check("kvq_quantize_pack", st)
+
+
+def kvq_decode_attention(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed, v_packed,
+                         packed_row_stride_bytes: int, n_packed_tokens: int, k_res_fp16,
+                         v_res_fp16, res_capacity: int, n_res: int, sm_scale: float,
+                         num_splits: int, part_o, part_lse, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_packed),
+                                    _ptr(v_packed), packed_row_stride_bytes, n_packed_tokens,
+                                    _ptr(k_res_fp16), _ptr(v_res_fp16), res_capacity, n_res,
+                                    float(sm_scale), num_splits, _ptr(part_o), _ptr(part_lse),
+                                    _stream(stream, q_fp16))
+    _check("kvq_decode_attention", st)
+
+
+def kvq_combine(part_o, part_lse, B: int, Hq: int, head_dim: int, num_splits: int, out,
+                out_dtype: int = KVQ_OUT_F32, stream=None):
+    st = lib().kvq_combine(_ptr(part_o), _ptr(part_lse), B, Hq, head_dim, num_splits, _ptr(out),
+                           out_dtype, _stream(stream, part_o))
+    _check("kvq_combine", st)
+
+
+def kvq_append_residual(k_new, v_new, k_res, v_res, B: int, Hkv: int, head_dim: int,
+                        res_capacity: int, slot: int, stream=None):
+    st = lib().kvq_append_residual(_ptr(k_new), _ptr(v_new), _ptr(k_res), _ptr(v_res), B, Hkv,
+                                   head_dim, res_capacity, slot, _stream(stream, k_new))
+    _check("kvq_append_residual", st)
+
+
+def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
+    """Same rule as the header's kvq_suggest_splits."""
+    rows = B * Hkv
+    tiles = n_tokens // 32 + 1
+    want = (4 * cu_count + rows - 1) // rows
+    cap = tiles // 4 + 1
+    return int(max(1, min(256, min(want, cap))))

@@ -1,0 +1,236 @@
+/*
+ * kvq.h -- C ABI of libkvq: decode-step attention read directly from a low-bit,
+ * group-wise, asymmetrically quantized KV cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources (web pages; cited by title and section):
+ *   [BitDecoding] "Tensor Core加速的低比特KV缓存解码系统" (cyqw.cn)
+ *   [InnerQ]      "KV缓存量化技术InnerQ：提升大模型推理效率" (jsqmd.com)
+ *   [3-bit blog]  "3-bit KV缓存量化：大模型推理功耗与带宽优化核心技术" (yfxerp.com)
+ *
+ * Conventions for every call:
+ *   - All data pointers are DEVICE pointers, owned by the caller. The library never
+ *     allocates, frees or synchronizes; work is enqueued on `stream` and the call
+ *     returns at once. A NULL stream is the default stream.
+ *   - Arguments are validated on the host before anything is launched; on error nothing
+ *     is enqueued and a negative kvq_status is returned. A launch the runtime rejects
+ *     returns KVQ_ERR_LAUNCH. No C++ exception crosses this interface.
+ *   - The library keeps no mutable global state: calls are thread-safe and re-entrant.
+ *     Calls on one stream run in order; the caller orders calls across streams.
+ *   - Device pointers must be 64-byte aligned (KVQ_ERR_ALIGN otherwise). [BitDecoding]
+ *     sec. 5.1 asks for aligned KV pointers; [InnerQ] sec. 3.2 aligns parameters to 64 B.
+ *   - Non-finite fp16 inputs (inf, NaN) give undefined results.
+ *
+ * ---------------------------------------------------------------------------------
+ * Packed cache format ([InnerQ] sec. 2.1 groups along head_dim, sec. 3.2 layout)
+ * ---------------------------------------------------------------------------------
+ * A "row" is the K (or the V) cache of one (batch, kv-head). A row is a sequence of
+ * blocks of 128 tokens; block j of row r starts at base + r*row_stride + j*block_bytes.
+ * Inside a block (d = head_dim, G = 32, ng = d/G groups per token, b = bits):
+ *
+ *   codes  [128 tokens][ng groups][4*b bytes]   at offset 0
+ *          The 32 codes of a group form one little-endian (32*b)-bit word: code i sits
+ *          at bits [b*i, b*i + b) (LSB first; 3-bit codes 10 and 21 straddle 32-bit
+ *          words). At 4 bits a group is one 128-bit word ([InnerQ] sec. 3.2); at 3 bits
+ *          it is three uint32; at 2 bits two uint32.
+ *   sz     [128 tokens][ng groups]{fp16 scale, fp16 zero}   at offset align64(codes)
+ *          4 bytes per group: scale in the low half, zero in the high half.
+ *   flags  [128*ng bits], bit (token*ng + group), 1 = asymmetric, 0 = symmetric;
+ *          present only when fmt.hybrid != 0, at offset align64(sz end).
+ *   block_bytes = align64(end of the last region). At d = 128: 4-bit 10240 B,
+ *   3-bit 8192 B, 2-bit 6144 B (hybrid +64 B).
+ *
+ * A value decodes as  x = zero + code * scale  ([InnerQ] sec. 3.1) in both modes.
+ *
+ * Quantizer, per group x[0..31] (fp16), N = 2^b - 1, every step one IEEE binary32
+ * operation rounded to nearest even ([BitDecoding] sec. 2.1 scale and round;
+ * [3-bit blog] sec. 2.3 clip):
+ *   mn = min(x) + 0, mx = max(x) + 0            (-0.0 taken as +0.0)
+ *   scale = fp16((mx - mn) / N), zero = fp16(mn)  (zero is exact)
+ *   code_i = 0 if scale == 0, else min(N, round_half_away((x_i - zero) / scale))
+ *   (the stored fp16 scale is the one used to compute the codes).
+ * Hybrid ([InnerQ] sec. 2.2): a symmetric candidate with s = fp16(max|x| / (2^(b-1)-1)),
+ *   code_i = 2^(b-1) + clamp(round_half_away(x_i / s), -(2^(b-1)-1), 2^(b-1)-1)
+ *   (2^(b-1) when s == 0) and zero = -2^(b-1) * s (not eligible if that overflows fp16);
+ *   its error e_i = x_i - fma(code_i, scale, zero) is summed as e_i^2 in binary32 in a
+ *   balanced pairwise tree over channel order; the symmetric candidate is kept only
+ *   when its sum is strictly below the asymmetric one's; the flag records the choice.
+ *
+ * ---------------------------------------------------------------------------------
+ * Residual / sink window ([BitDecoding] sec. 2.2; [InnerQ] sec. 2.3)
+ * ---------------------------------------------------------------------------------
+ * fp16 K and V buffers [B][Hkv][res_capacity][head_dim], token-major. Slots
+ * 0..n_res-1 are attended in full precision next to the packed tokens. Slot order does
+ * not matter to the result (no mask). When the window is full, the caller quantizes it
+ * into the next packed block with kvq_quantize_pack and starts again at slot 0.
+ *
+ * ---------------------------------------------------------------------------------
+ * Split-K partials
+ * ---------------------------------------------------------------------------------
+ * The token sequence of a (batch, kv-head) is packed tokens 0..n_packed-1 then the
+ * residual slots 0..n_res-1. Packed tokens form 32-token tiles (NT = n_packed/32).
+ * With num_splits S > 1 and n_res > 0, split S-1 holds exactly the residual and splits
+ * 0..S-2 share the tiles; otherwise all S splits share the tiles and split S-1 also takes
+ * the residual. Of the Sp tile-sharing splits, split s gets tiles [s*NT/Sp, (s+1)*NT/Sp)
+ * (integer division). A split with no token has lse = -inf and o = 0.
+ *   part_o  [B][Hq][S][head_dim] fp32: sum_t p_t v_t / sum_t p_t over the split's tokens
+ *   part_lse[B][Hq][S] fp32: m + ln(sum_t e^(l_t - m)), l_t = sm_scale * q . k_t
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_NULL = -1,        /* a required pointer is NULL */
+    KVQ_ERR_SHAPE = -2,       /* sizes or strides out of range or inconsistent */
+    KVQ_ERR_UNSUPPORTED = -3, /* valid request that this build does not implement */
+    KVQ_ERR_ALIGN = -4,       /* pointer or stride not aligned as required */
+    KVQ_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
+} kvq_status;
+
+typedef struct {
+    int32_t bits;         /* 2, 3 or 4 */
+    int32_t head_dim;     /* 128 (multiple of 32 in the format; kernels take 128) */
+    int32_t group;        /* must be 32 */
+    int32_t hybrid;       /* 0: asymmetric only; 1: per-group sym/asym choice + flag bit */
+    int32_t block_tokens; /* must be 128: packed block = flush unit = residual capacity */
+} kvq_format;
+
+typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1 } kvq_out_dtype;
+
+/* ---- size helpers (header-only) ---- */
+static inline int64_t kvq_align64(int64_t v) { return (v + 63) / 64 * 64; }
+static inline int64_t kvq_codes_bytes(const kvq_format *f)
+{
+    return (int64_t)f->block_tokens * f->head_dim * f->bits / 8;
+}
+static inline int64_t kvq_sz_offset(const kvq_format *f) { return kvq_align64(kvq_codes_bytes(f)); }
+static inline int64_t kvq_sz_bytes(const kvq_format *f)
+{
+    return (int64_t)f->block_tokens * (f->head_dim / f->group) * 4;
+}
+static inline int64_t kvq_flag_offset(const kvq_format *f)
+{
+    return kvq_align64(kvq_sz_offset(f) + kvq_sz_bytes(f));
+}
+static inline int64_t kvq_flag_bytes(const kvq_format *f)
+{
+    return f->hybrid ? ((int64_t)f->block_tokens * (f->head_dim / f->group) + 7) / 8 : 0;
+}
+static inline int64_t kvq_block_bytes(const kvq_format *f)
+{
+    return kvq_align64(kvq_flag_offset(f) + kvq_flag_bytes(f));
+}
+/* A split count that gives a few thousand workgroups' worth of tiles on `cu_count` CUs:
+   enough splits that B*Hkv*S fills the chip several times, none with fewer than 4 tiles. */
+static inline int32_t kvq_suggest_splits(int32_t B, int32_t Hkv, int32_t n_tokens,
+                                         int32_t cu_count)
+{
+    int64_t rows = (int64_t)B * Hkv;
+    int64_t tiles = n_tokens / 32 + 1;
+    int64_t want = (4LL * cu_count + rows - 1) / rows;     /* ~4 workgroups per CU */
+    int64_t cap = tiles / 4 + 1;
+    int64_t s = want < cap ? want : cap;
+    if (s < 1) s = 1;
+    if (s > 256) s = 256;
+    return (int32_t)s;
+}
+static inline const char *kvq_status_string(kvq_status s)
+{
+    switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_ERR_NULL: return "null pointer";
+    case KVQ_ERR_SHAPE: return "bad shape or stride";
+    case KVQ_ERR_UNSUPPORTED: return "unsupported format or shape";
+    case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
+    case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    }
+    return "unknown status";
+}
+
+/*
+ * kvq_quantize_pack -- quantize fp16 tokens and write them as packed blocks.
+ * [BitDecoding] sec. 2.1 (scale/zero/round), sec. 3.1 (register-only quantize with a
+ * cross-lane min/max reduction); [InnerQ] sec. 2.1-2.2 (groups along head_dim, hybrid
+ * mode and flag); [3-bit blog] sec. 2.3 (clip), sec. 3.2 (fp16 K/V -> packed + scale/zero).
+ *
+ *   src_fp16        fp16 [n_rows][..][head_dim]: token t of row r at
+ *                   src + r*src_row_stride + t*src_tok_stride (elements); channels contiguous.
+ *                   Strides must be multiples of 8 elements (16-byte token rows).
+ *   n_rows          rows to quantize (e.g. B*Hkv for the K or the V cache), >= 1
+ *   n_tokens        tokens per row, a positive multiple of 128
+ *   dst_packed      packed rows; row r at dst + r*dst_row_stride_bytes
+ *   dst_row_stride_bytes  >= (dst_first_block + n_tokens/128) * kvq_block_bytes(fmt),
+ *                   multiple of 64
+ *   dst_first_block first block written in every row (the flush of a full residual window
+ *                   writes block n_packed/128)
+ * Writes blocks [dst_first_block, dst_first_block + n_tokens/128) of every row, all bytes
+ * of each block (codes, scale/zero, flags). Deterministic: equal inputs give equal bytes.
+ */
+kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                             int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                             void *dst_packed, int64_t dst_row_stride_bytes,
+                             int32_t dst_first_block, hipStream_t stream);
+
+/*
+ * kvq_decode_attention -- split-K partials of one decode step.
+ * [BitDecoding] sec. 2.2 (fp16 residual block next to the packed cache), sec. 2.3 (query
+ * rows of one GQA group processed together; dequantize while computing); [InnerQ] sec. 3.1
+ * (fused dequantize + dot product, scale/zero staged on chip), sec. 2.3 (sink/recent
+ * windows at full precision).
+ *
+ *   q_fp16          [B][Hq][head_dim]; head h reads kv-head h / (Hq/Hkv)
+ *   k_packed, v_packed   packed rows [B*Hkv], row b*Hkv + kvh at base + row*packed_row_stride_bytes
+ *   n_packed_tokens multiple of 128, >= 0; the row stride must hold n_packed/128 blocks
+ *   k_res_fp16, v_res_fp16  [B][Hkv][res_capacity][head_dim] (may be NULL when n_res == 0)
+ *   n_res           0..res_capacity; n_packed + n_res must be > 0
+ *   sm_scale        softmax scale (1/sqrt(head_dim) for standard attention)
+ *   num_splits      S >= 1 (at most 1024); see "Split-K partials" above for the token split
+ *   part_o, part_lse  fp32 outputs as described above
+ * Supported: bits 2/3/4, head_dim 128, 1 <= Hq/Hkv <= 16.
+ */
+kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                int32_t Hq, int32_t Hkv, const void *k_packed,
+                                const void *v_packed, int64_t packed_row_stride_bytes,
+                                int32_t n_packed_tokens, const void *k_res_fp16,
+                                const void *v_res_fp16, int32_t res_capacity, int32_t n_res,
+                                float sm_scale, int32_t num_splits, float *part_o,
+                                float *part_lse, hipStream_t stream);
+
+/*
+ * kvq_combine -- merge the split partials into the attention output (the log-sum-exp
+ * merge of split-K flash-decoding, the FP16 baseline named in [BitDecoding] sec. 4.2):
+ *   M = max_s lse_s, w_s = e^(lse_s - M), out = sum_s w_s o_s / sum_s w_s.
+ * Splits with lse = -inf weigh 0. Every (b, h) must have at least one non-empty split.
+ *   out             [B][Hq][head_dim], fp32 (KVQ_OUT_F32) or fp16 rounded to nearest even
+ *                   from the fp32 result (KVQ_OUT_F16)
+ */
+kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
+                       int32_t head_dim, int32_t num_splits, void *out, int32_t out_dtype,
+                       hipStream_t stream);
+
+/*
+ * kvq_append_residual -- write one new fp16 token per (batch, kv-head) into residual slot
+ * `slot` of the K and V windows ([InnerQ] sec. 2.3: new tokens always enter the recent
+ * window).
+ *   k_new, v_new    fp16 [B][Hkv][head_dim]
+ *   k_res, v_res    fp16 [B][Hkv][res_capacity][head_dim]
+ *   0 <= slot < res_capacity
+ */
+kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res, void *v_res,
+                               int32_t B, int32_t Hkv, int32_t head_dim, int32_t res_capacity,
+                               int32_t slot, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,151 @@
+"""Host-only checks of the C ABI: the library loads, exports every call include/kvq.h
+declares, and rejects bad arguments before launching anything (these calls never reach a
+kernel launch, so they run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+from bit_kv_cache_pack_amd import kvq as K
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+A = 1 << 20          # a fake, 64-byte aligned "device" address (never dereferenced)
+MIS = A + 2          # misaligned
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^kvq_status\s+(kvq_\w+)\s*\(", src, re.M)))
+
+
+def test_library_exports_every_declared_call():
+    names = _declared()
+    assert names == sorted(K.EXPORTED)
+    L = K.lib()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def _fmt(**kw):
+    f = dict(bits=4, head_dim=128, group=32, hybrid=0, block_tokens=128)
+    f.update(kw)
+    return K.kvq_format(**f)
+
+
+def _qp(fmt=None, src=A, rows=2, T=256, rs=256 * 128, ts=128, dst=A, dstride=2 * 10240, fb=0):
+    f = _fmt() if fmt is None else fmt
+    return K.lib().kvq_quantize_pack(C.byref(f) if f is not False else None, src, rows, T, rs, ts,
+                                     dst, dstride, fb, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=False), K.KVQ_ERR_NULL),
+    (dict(fmt=_fmt(bits=5)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(bits=1)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(group=16)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(block_tokens=64)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(hybrid=2)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(head_dim=64)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(fmt=_fmt(head_dim=100)), K.KVQ_ERR_SHAPE),
+    (dict(src=None), K.KVQ_ERR_NULL),
+    (dict(dst=None), K.KVQ_ERR_NULL),
+    (dict(rows=0), K.KVQ_ERR_SHAPE),
+    (dict(T=100), K.KVQ_ERR_SHAPE),
+    (dict(T=0), K.KVQ_ERR_SHAPE),
+    (dict(fb=-1), K.KVQ_ERR_SHAPE),
+    (dict(ts=64), K.KVQ_ERR_SHAPE),
+    (dict(ts=132), K.KVQ_ERR_ALIGN),
+    (dict(rs=256 * 128 + 4), K.KVQ_ERR_ALIGN),
+    (dict(src=MIS), K.KVQ_ERR_ALIGN),
+    (dict(dst=MIS), K.KVQ_ERR_ALIGN),
+    (dict(dstride=2 * 10240 + 32), K.KVQ_ERR_ALIGN),
+    (dict(dstride=10240), K.KVQ_ERR_SHAPE),          # 2 blocks do not fit
+    (dict(fb=1, dstride=2 * 10240), K.KVQ_ERR_SHAPE),
+])
+def test_quantize_pack_rejects(kw, status):
+    assert _qp(**kw) == status
+
+
+def _dec(fmt=None, q=A, B=1, Hq=8, Hkv=2, kp=A, vp=A, stride=10240, n_packed=128, kr=A, vr=A,
+         cap=128, n_res=4, sm=0.088, S=4, po=A, pl=A):
+    f = _fmt() if fmt is None else fmt
+    return K.lib().kvq_decode_attention(C.byref(f), q, B, Hq, Hkv, kp, vp, stride, n_packed, kr,
+                                        vr, cap, n_res, sm, S, po, pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=_fmt(bits=7)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(po=None), K.KVQ_ERR_NULL),
+    (dict(pl=None), K.KVQ_ERR_NULL),
+    (dict(kp=None), K.KVQ_ERR_NULL),
+    (dict(vr=None), K.KVQ_ERR_NULL),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(B=0), K.KVQ_ERR_SHAPE),
+    (dict(n_packed=100), K.KVQ_ERR_SHAPE),
+    (dict(n_packed=-128), K.KVQ_ERR_SHAPE),
+    (dict(n_res=129), K.KVQ_ERR_SHAPE),
+    (dict(n_res=-1), K.KVQ_ERR_SHAPE),
+    (dict(n_packed=0, n_res=0), K.KVQ_ERR_SHAPE),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(S=1025), K.KVQ_ERR_SHAPE),
+    (dict(sm=float("nan")), K.KVQ_ERR_SHAPE),
+    (dict(sm=float("inf")), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),   # 17 query heads per kv head
+    (dict(stride=10240 + 8), K.KVQ_ERR_ALIGN),
+    (dict(n_packed=256), K.KVQ_ERR_SHAPE),          # row stride holds one block only
+    (dict(kp=MIS), K.KVQ_ERR_ALIGN),
+    (dict(kr=MIS), K.KVQ_ERR_ALIGN),
+    (dict(q=MIS), K.KVQ_ERR_ALIGN),
+    (dict(po=MIS), K.KVQ_ERR_ALIGN),
+])
+def test_decode_rejects(kw, status):
+    assert _dec(**kw) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A, 1, 8, 128, 4, A, 0), K.KVQ_ERR_NULL),
+    ((A, A, 1, 8, 128, 4, None, 0), K.KVQ_ERR_NULL),
+    ((A, A, 0, 8, 128, 4, A, 0), K.KVQ_ERR_SHAPE),
+    ((A, A, 1, 8, 128, 0, A, 0), K.KVQ_ERR_SHAPE),
+    ((A, A, 1, 8, 128, 2000, A, 0), K.KVQ_ERR_SHAPE),
+    ((A, A, 1, 8, 64, 4, A, 0), K.KVQ_ERR_UNSUPPORTED),
+    ((A, A, 1, 8, 128, 4, A, 3), K.KVQ_ERR_UNSUPPORTED),
+    ((MIS, A, 1, 8, 128, 4, A, 0), K.KVQ_ERR_ALIGN),
+    ((A, A, 1, 8, 128, 4, MIS, 1), K.KVQ_ERR_ALIGN),
+])
+def test_combine_rejects(args, status):
+    assert K.lib().kvq_combine(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((None, A, A, A, 1, 2, 128, 128, 0), K.KVQ_ERR_NULL),
+    ((A, A, A, A, 1, 2, 128, 128, 128), K.KVQ_ERR_SHAPE),
+    ((A, A, A, A, 1, 2, 128, 128, -1), K.KVQ_ERR_SHAPE),
+    ((A, A, A, A, 0, 2, 128, 128, 0), K.KVQ_ERR_SHAPE),
+    ((A, A, A, A, 1, 2, 96, 128, 0), K.KVQ_ERR_UNSUPPORTED),
+    ((A, MIS, A, A, 1, 2, 128, 128, 0), K.KVQ_ERR_ALIGN),
+])
+def test_append_rejects(args, status):
+    assert K.lib().kvq_append_residual(*args, None) == status
+
+
+@pytest.mark.parametrize("bits,hybrid", [(2, 0), (2, 1), (3, 0), (3, 1), (4, 0), (4, 1)])
+def test_format_sizes_agree_with_oracle_restatement(oracle_mod, bits, hybrid):
+    """The header's size helpers (mirrored in Python) and the oracle's independent
+    restatement of the block layout give the same offsets."""
+    f = K.Format(bits, 128, bool(hybrid))
+    o = oracle_mod.Format(bits, 128, bool(hybrid))
+    assert (f.codes_bytes, f.sz_offset, f.sz_bytes, f.flag_offset, f.flag_bytes, f.block_bytes) == \
+        (o.codes_bytes, o.sz_offset, o.sz_bytes, o.flag_offset, o.flag_bytes, o.block_bytes)
+
+
+def test_suggest_splits_bounds():
+    for B, Hkv, n in [(1, 8, 32768), (8, 8, 32768), (1, 8, 131072), (64, 40, 4096), (1, 2, 1024),
+                      (1, 1, 1)]:
+        s = K.suggest_splits(B, Hkv, n)
+        assert 1 <= s <= 256
+        assert s <= n // 32 // 4 + 1

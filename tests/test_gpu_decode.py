@@ -1,0 +1,278 @@
+"""GPU parity of kvq_decode_attention + kvq_combine against the fp64 CPU oracle.
+
+Bar: max |gpu - oracle| <= 2e-3 and ||gpu - oracle||_2 / ||oracle||_2 <= 1e-3 over the
+whole output. The oracle attends over the packed cache it built itself from the same
+seeded fp16 inputs (the packed bytes are checked equal separately), plus the same fp16
+residual window."""
+import numpy as np
+import pytest
+import torch
+
+import synth_inputs as S
+from bit_kv_cache_pack_amd import kvq as K
+
+pytestmark = pytest.mark.gpu
+
+SM = float(np.float32(1.0 / np.sqrt(128.0)))
+
+
+def _f16(a):
+    return np.asarray(a, np.float32).astype(np.float16)
+
+
+def _case(rng, B, Hq, Hkv, n_packed, n_res, dist="normal", scale=1.0, cap=128):
+    k = _f16(rng.standard_normal((B, Hkv, n_packed + n_res, 128)) * scale)
+    v = _f16(rng.standard_normal((B, Hkv, n_packed + n_res, 128)) * scale)
+    if dist == "t5":
+        k = _f16(rng.standard_t(5, size=k.shape) * scale)
+        v = _f16(rng.standard_t(5, size=v.shape) * scale)
+    q = _f16(rng.standard_normal((B, Hq, 128)))
+    kr = np.zeros((B, Hkv, cap, 128), np.float16)
+    vr = np.zeros_like(kr)
+    kr[:, :, :n_res] = k[:, :, n_packed:]
+    vr[:, :, :n_res] = v[:, :, n_packed:]
+    return q, k[:, :, :n_packed], v[:, :, :n_packed], kr, vr
+
+
+def _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, dist="normal", scale=1.0,
+         seed=0, cap=128, check_partials=True):
+    from gpu_common import assert_close, dev, gpu_decode, gpu_quantize
+    O = oracle_mod
+    rng = np.random.default_rng(seed)
+    q, ksrc, vsrc, kr, vr = _case(rng, B, Hq, Hkv, n_packed, n_res, dist, scale, cap)
+    fmt = K.Format(bits, 128, hybrid)
+    ofmt = O.Format(bits, 128, hybrid)
+    rows = B * Hkv
+    print(f"[decode] bits={bits} hybrid={hybrid} B={B} Hq={Hq} Hkv={Hkv} n_packed={n_packed} "
+          f"n_res={n_res} S={S_} seed={seed}", flush=True)
+    if n_packed:
+        kp_ref = O.quantize_pack(ofmt, ksrc.reshape(rows, n_packed, 128))
+        vp_ref = O.quantize_pack(ofmt, vsrc.reshape(rows, n_packed, 128))
+        kp = gpu_quantize(fmt, ksrc.reshape(rows, n_packed, 128))
+        vp = gpu_quantize(fmt, vsrc.reshape(rows, n_packed, 128))
+        assert np.array_equal(kp.cpu().numpy(), kp_ref)
+        assert np.array_equal(vp.cpu().numpy(), vp_ref)
+    else:
+        kp_ref = vp_ref = np.zeros((rows, 0), np.uint8)
+        kp = vp = None
+    qd, krd, vrd = dev(q), dev(kr), dev(vr)
+    out, po, pl = gpu_decode(fmt, qd, Hkv, kp, vp, n_packed, krd, vrd, n_res, S_, sm=SM)
+    torch.cuda.synchronize()
+    ref = O.attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, sm=SM)
+    res = assert_close(out.cpu().numpy(), ref, "attention")
+    if check_partials:
+        rpo, rpl = O.split_attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, S=S_,
+                                     sm=SM)
+        gpl = pl.cpu().numpy()
+        gpo = po.cpu().numpy()
+        empty = np.isneginf(rpl)
+        assert np.array_equal(np.isneginf(gpl), empty), "empty splits differ"
+        assert np.max(np.abs(gpl[~empty] - rpl[~empty])) < 1e-3
+        assert np.all(gpo[empty] == 0)
+        assert_close(gpo[~empty], rpo[~empty], "partials")
+    return res
+
+
+CASES = [
+    # bits, hybrid, B, Hq, Hkv, n_packed, n_res, S
+    (4, False, 1, 8, 2, 896, 128, 1),
+    (4, False, 1, 8, 2, 896, 128, 7),
+    (4, False, 2, 8, 2, 640, 77, 3),
+    (4, False, 1, 4, 1, 256, 1, 2),
+    (4, False, 2, 4, 4, 384, 0, 5),        # gq 1, no residual
+    (4, False, 1, 4, 2, 384, 33, 4),       # gq 2
+    (4, False, 1, 6, 2, 256, 100, 3),      # gq 3 (tail launch only)
+    (4, False, 1, 16, 2, 256, 50, 3),      # gq 8 (two head chunks)
+    (4, False, 1, 10, 2, 256, 50, 2),      # gq 5 (chunk + tail)
+    (4, False, 1, 32, 2, 128, 20, 2),      # gq 16
+    (3, False, 1, 8, 2, 640, 128, 4),
+    (3, False, 2, 4, 4, 256, 31, 9),
+    (2, False, 1, 8, 2, 640, 128, 4),
+    (2, True, 2, 8, 2, 640, 128, 5),
+    (3, True, 1, 8, 2, 384, 64, 3),
+    (4, True, 1, 8, 2, 384, 64, 3),
+    (4, False, 1, 8, 2, 256, 128, 64),     # more splits than tiles: empty splits
+    (4, False, 1, 8, 2, 0, 128, 1),        # all tokens in the fp16 window
+    (4, False, 1, 8, 2, 0, 5, 3),          # tiny residual only, empty packed splits
+    (4, False, 1, 8, 2, 128, 0, 1),        # one block, one split
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: "b{}h{}_B{}_{}x{}_P{}_R{}_S{}".format(*c))
+def test_decode_small(oracle_mod, case):
+    bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_ = case
+    _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, seed=sum(case))
+
+
+@pytest.mark.parametrize("dist,scale", [("t5", 1.0), ("normal", 4.0), ("normal", 0.05)])
+def test_decode_value_ranges(oracle_mod, dist, scale):
+    _run(oracle_mod, 4, False, 1, 8, 2, 640, 128, 5, dist=dist, scale=scale, seed=7)
+    _run(oracle_mod, 2, True, 1, 8, 2, 640, 128, 5, dist=dist, scale=scale, seed=8)
+
+
+def test_decode_residual_capacity_not_multiple_of_tile(oracle_mod):
+    _run(oracle_mod, 4, False, 1, 8, 2, 256, 70, 3, cap=100, seed=9)
+
+
+def test_decode_single_token(oracle_mod):
+    """One fp16 token: the output is that token's value row."""
+    from gpu_common import dev, gpu_decode
+    rng = np.random.default_rng(10)
+    q = _f16(rng.standard_normal((1, 4, 128)))
+    kr = _f16(rng.standard_normal((1, 1, 128, 128)))
+    vr = _f16(rng.standard_normal((1, 1, 128, 128)))
+    print("[decode single token]", flush=True)
+    out, _, _ = gpu_decode(K.Format(4), dev(q), 1, None, None, 0, dev(kr), dev(vr), 1, 1)
+    got = out.cpu().numpy()
+    assert np.max(np.abs(got - vr[0, 0, 0].astype(np.float32)[None, None])) <= 1e-6
+
+
+def test_combine_alone_matches_oracle(oracle_mod):
+    """kvq_combine on partials made by the oracle (fp64 -> fp32), against the oracle merge."""
+    from gpu_common import DEV, assert_close
+    O = oracle_mod
+    rng = np.random.default_rng(11)
+    B, Hq, S_ = 2, 8, 37
+    po = rng.standard_normal((B, Hq, S_, 128))
+    pl = rng.standard_normal((B, Hq, S_)) * 5
+    pl[0, 0, 3:] = -np.inf
+    pl[1, 2, ::2] = -np.inf
+    po[np.isneginf(pl)] = 0.0
+    ref = O.combine(po, pl)
+    pot = torch.from_numpy(po.astype(np.float32)).to(DEV)
+    plt = torch.from_numpy(pl.astype(np.float32)).to(DEV)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    out16 = torch.empty((B, Hq, 128), dtype=torch.float16, device=DEV)
+    print("[combine alone]", flush=True)
+    K.kvq_combine(pot, plt, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
+    K.kvq_combine(pot, plt, B, Hq, 128, S_, out16, K.KVQ_OUT_F16)
+    got = out.cpu().numpy()
+    assert np.max(np.abs(got - ref)) < 1e-5
+    # fp16 output is the round-to-nearest-even of the fp32 output, exactly
+    assert np.array_equal(out16.cpu().numpy(), got.astype(np.float16))
+    assert_close(got, ref)
+
+
+def test_decode_fp16_output(oracle_mod):
+    from gpu_common import dev, gpu_decode, gpu_quantize
+    rng = np.random.default_rng(12)
+    q, ksrc, vsrc, kr, vr = _case(rng, 1, 8, 2, 384, 50)
+    fmt = K.Format(4)
+    kp = gpu_quantize(fmt, ksrc.reshape(2, 384, 128))
+    vp = gpu_quantize(fmt, vsrc.reshape(2, 384, 128))
+    print("[decode fp16 out]", flush=True)
+    o32, _, _ = gpu_decode(fmt, dev(q), 2, kp, vp, 384, dev(kr), dev(vr), 50, 3)
+    o16, _, _ = gpu_decode(fmt, dev(q), 2, kp, vp, 384, dev(kr), dev(vr), 50, 3,
+                           out_dtype=K.KVQ_OUT_F16)
+    assert np.array_equal(o16.cpu().numpy(), o32.cpu().numpy().astype(np.float16))
+
+
+def test_decode_rerun_is_deterministic():
+    from gpu_common import dev, gpu_decode, gpu_quantize
+    rng = np.random.default_rng(13)
+    q, ksrc, vsrc, kr, vr = _case(rng, 1, 8, 2, 1024, 128)
+    fmt = K.Format(4)
+    kp = gpu_quantize(fmt, ksrc.reshape(2, 1024, 128))
+    vp = gpu_quantize(fmt, vsrc.reshape(2, 1024, 128))
+    print("[decode determinism]", flush=True)
+    a = gpu_decode(fmt, dev(q), 2, kp, vp, 1024, dev(kr), dev(vr), 128, 9)[0]
+    b = gpu_decode(fmt, dev(q), 2, kp, vp, 1024, dev(kr), dev(vr), 128, 9)[0]
+    assert torch.equal(a, b)
+
+
+# ------------------------------------------------------------------ full workloads ----
+
+def _full(oracle_mod, name):
+    from gpu_common import assert_close, bench_splits, dev, gpu_decode, gpu_quantize
+    O = oracle_mod
+    wl = S.WORKLOADS[name]
+    print(f"[decode full] {name}: generating inputs", flush=True)
+    x = S.make_inputs(wl)
+    kps, vps = x.packed_src()
+    kr, vr = x.residual()
+    fmt = K.Format(wl.bits, 128, wl.hybrid)
+    ofmt = O.Format(wl.bits, 128, wl.hybrid)
+    rows = wl.B * wl.Hkv
+    kps = np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128))
+    vps = np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128))
+    print(f"[decode full] {name}: quantize on GPU", flush=True)
+    kp = gpu_quantize(fmt, kps)
+    vp = gpu_quantize(fmt, vps)
+    S_ = bench_splits(wl)
+    print(f"[decode full] {name}: decode S={S_}", flush=True)
+    out, _, _ = gpu_decode(fmt, dev(x.q), wl.Hkv, kp, vp, wl.n_packed, dev(kr), dev(vr), wl.n_res,
+                           S_, sm=SM)
+    got = out.cpu().numpy()
+    del kp, vp
+    print(f"[decode full] {name}: oracle", flush=True)
+    kp_ref = O.quantize_pack(ofmt, kps)
+    vp_ref = O.quantize_pack(ofmt, vps)
+    ref = O.attention(ofmt, x.q, wl.Hkv, kp_ref, vp_ref, wl.n_packed, kr, vr, wl.n_res, sm=SM)
+    ma, rl = assert_close(got, ref, name)
+    print(f"[decode full] {name}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name", ["tiny", "llama8b_32k", "batch8_2bit_hybrid", "long_128k_3bit"])
+def test_decode_full_workload(oracle_mod, name):
+    _full(oracle_mod, name)
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(600)
+def test_append_flush_loop_full(oracle_mod):
+    """B64 x 40 heads, L 4096: each step appends one token per sequence; when the 128-slot
+    window is full it is quantized into the next packed block first. Checked against the
+    oracle (own packing of the same tokens) at several steps, including both flushes."""
+    from gpu_common import DEV, assert_close, bench_splits, dev, gpu_decode
+    O = oracle_mod
+    wl = S.WORKLOADS["mha_b64_append"]
+    print("[append loop] generating inputs", flush=True)
+    x = S.make_inputs(wl)
+    rows = wl.B * wl.Hkv
+    fmt = K.Format(wl.bits)
+    ofmt = O.Format(wl.bits)
+    bb = fmt.block_bytes
+    steps = 257
+    cap_blocks = wl.n_packed // 128 + 3
+    kps, vps = x.packed_src()
+    kps = np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128))
+    vps = np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128))
+    kp_ref = O.quantize_pack(ofmt, kps, n_blocks_capacity=cap_blocks)
+    vp_ref = O.quantize_pack(ofmt, vps, n_blocks_capacity=cap_blocks)
+    kp = torch.zeros((rows, cap_blocks * bb), dtype=torch.uint8, device=DEV)
+    vp = torch.zeros_like(kp)
+    for src, dst in ((kps, kp), (vps, vp)):
+        K.kvq_quantize_pack(fmt, dev(src), rows, wl.n_packed, wl.n_packed * 128, 128, dst,
+                            cap_blocks * bb, 0)
+    kr, vr = x.residual()                       # full window (128 recent tokens)
+    krd, vrd = dev(kr), dev(vr)
+    n_packed, r = wl.n_packed, wl.n_res
+    S_ = bench_splits(wl)
+    check_at = {1, 2, 64, 128, 129, 256, 257}
+    for step in range(1, steps + 1):
+        kn, vn, q = S.append_step_inputs(x.rng, wl)
+        if r == 128:                            # flush the full window
+            K.kvq_quantize_pack(fmt, krd, rows, 128, 128 * 128, 128, kp, cap_blocks * bb,
+                                n_packed // 128)
+            K.kvq_quantize_pack(fmt, vrd, rows, 128, 128 * 128, 128, vp, cap_blocks * bb,
+                                n_packed // 128)
+            O.quantize_pack(ofmt, kr.reshape(rows, 128, 128), first_block=n_packed // 128, dst=kp_ref)
+            O.quantize_pack(ofmt, vr.reshape(rows, 128, 128), first_block=n_packed // 128, dst=vp_ref)
+            n_packed += 128
+            r = 0
+        K.kvq_append_residual(dev(kn), dev(vn), krd, vrd, wl.B, wl.Hkv, 128, 128, r)
+        kr[:, :, r] = kn
+        vr[:, :, r] = vn
+        r += 1
+        out, _, _ = gpu_decode(fmt, dev(q), wl.Hkv, kp, vp, n_packed, krd, vrd, r, S_, sm=SM)
+        if step in check_at:
+            print(f"[append loop] step {step}: n_packed={n_packed} r={r}", flush=True)
+            got = out.cpu().numpy()
+            ref = O.attention(ofmt, q, wl.Hkv, kp_ref, vp_ref, n_packed, kr, vr, r, sm=SM)
+            assert_close(got, ref, f"step {step}")
+    torch.cuda.synchronize()
+    assert np.array_equal(kp.cpu().numpy(), kp_ref)
+    assert np.array_equal(vp.cpu().numpy(), vp_ref)
+    assert np.array_equal(krd.cpu().numpy(), kr)
