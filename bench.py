@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's suggestion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copies", type=int, default=0,
+                    help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
     return ap.parse_args()
 
 
@@ -128,7 +130,7 @@ def main():
     K.kvq_quantize_pack(fmt, vps_d, rows, wl.n_packed, wl.n_packed * 128, 128, vp0, nb * bb, 0)
     del kps_d, vps_d
     step_bytes = wl.step_bytes()
-    copies = max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+    copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
     kr_d = torch.from_numpy(kr).to(dev)
     vr_d = torch.from_numpy(vr).to(dev)
     caches = [(kp0, vp0, kr_d, vr_d)] + [(kp0.clone(), vp0.clone(), kr_d.clone(), vr_d.clone())
@@ -140,32 +142,44 @@ def main():
     stream = torch.cuda.current_stream(dev)
     sptr = stream.cuda_stream
 
-    def step(i, ev=None):
+    def decode(i):
         kp, vp, krd, vrd = caches[i % copies]
-        if ev is not None:
-            ev[0].record(stream)
         K.kvq_decode_attention(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed, krd, vrd,
                                128, wl.n_res, sm, S_, part_o, part_lse, stream=sptr)
-        if ev is not None:
-            ev[1].record(stream)
+
+    def step(i):
+        decode(i)
         K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sptr)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # timed region: K whole steps back to back
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
     t_start.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
+    # decode kernel duration: HIP events around every launch, on the launch stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        evs[i][0].record(stream)
+        decode(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
     dec_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    # the same launches back to back (no events in between)
+    t_start.record(stream)
+    for i in range(args.steps):
+        decode(i)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    dec_b2b_ms = t_start.elapsed_time(t_end) / args.steps
 
     # flush (quantize the full 128-token window of every row, K and V) and append
     fl_reps = 50
@@ -223,6 +237,7 @@ def main():
         "data": "synthetic",
         "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
+        "decode_back_to_back_us": round(dec_b2b_ms * 1e3, 3),
         "flush_us": round(flush_ms * 1e3, 3),
         "append_us": round(append_ms * 1e3, 3),
         "step_us_with_append_and_amortized_flush": round((ms_per_step + append_ms + flush_ms / 128)

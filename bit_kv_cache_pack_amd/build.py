@@ -28,6 +28,9 @@ def compile_flags():
     return ["-O3", "-std=c++17", f"--offload-arch={ARCH}", "-fPIC",
             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
             "-fhip-fp32-correctly-rounded-divide-sqrt", "-Wall", "-Wno-unused-function",
+            # MFMA accumulators in ordinary VGPRs: the online-softmax rescale multiplies
+            # them every tile, which would otherwise copy them out of and back into AGPRs
+            "-mllvm", "-amdgpu-mfma-vgpr-form=1",
             "-I", INCLUDE, "-I", CSRC]
 
 

@@ -14,46 +14,62 @@
 namespace kvq {
 namespace {
 
-// One workgroup of 128 threads per (batch, head); thread d owns output channel d.
-// The lse row is read with uniform (scalar) loads; o rows are 512-byte coalesced reads.
+// One workgroup of 256 threads per (batch, head). Thread t owns output channels
+// 4*(t % 32) .. +3 for the splits s = t / 32, t / 32 + 8, ...; the eight partial sums of
+// each channel are then added through LDS. All loads of a thread are independent
+// 16-byte reads, so the whole partial block streams in parallel.
 template <bool F16>
-__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_lse, int S,
                                                       void *__restrict__ out)
 {
+    __shared__ float red_m[4];
+    __shared__ float4_t red_o[8][32];
+    __shared__ float red_w[8];
     const int64_t bh = blockIdx.x;
-    const int d = threadIdx.x;
+    const int t = threadIdx.x;
     const float *lse = part_lse + bh * S;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, lse[s]);
-    const float *o = part_o + bh * S * kHeadDim + d;
-    float acc = 0.0f, wsum = 0.0f;
-    int s = 0;
-    for (; s + 4 <= S; s += 4) {
-        float x[4], w[4];
+
+    float m = -INFINITY;
+    for (int s = t; s < S; s += 256) m = fmaxf(m, lse[s]);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            x[k] = o[(int64_t)(s + k) * kHeadDim];
-            const float ls = lse[s + k];
-            w[k] = ls == -INFINITY ? 0.0f : __expf(ls - M);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            acc = __builtin_fmaf(w[k], x[k], acc);
-            wsum += w[k];
-        }
-    }
-    for (; s < S; ++s) {
+    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
+    if ((t & 63) == 0) red_m[t >> 6] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
+
+    const int cq = t & 31, sg = t >> 5;
+    const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) + cq;
+    float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    float wsum = 0.0f;
+#pragma unroll 4
+    for (int s = sg; s < S; s += 8) {
         const float ls = lse[s];
         const float w = ls == -INFINITY ? 0.0f : __expf(ls - M);
-        acc = __builtin_fmaf(w, o[(int64_t)s * kHeadDim], acc);
+        const float4_t x = o[(int64_t)s * (kHeadDim / 4)];
+        acc += w * x;
         wsum += w;
     }
-    const float r = acc / wsum;
-    if (F16)
-        reinterpret_cast<_Float16 *>(out)[bh * kHeadDim + d] = (_Float16)r;
-    else
-        reinterpret_cast<float *>(out)[bh * kHeadDim + d] = r;
+    red_o[sg][cq] = acc;
+    if (cq == 0) red_w[sg] = wsum;
+    __syncthreads();
+    if (t < 32) {
+        float4_t tot = red_o[0][t];
+        float W = red_w[0];
+#pragma unroll
+        for (int k = 1; k < 8; ++k) {
+            tot += red_o[k][t];
+            W += red_w[k];
+        }
+        const float4_t r = tot / W;
+        if (F16) {
+            typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+            const half4_t h = {(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
+            reinterpret_cast<half4_t *>(out)[bh * (kHeadDim / 4) + t] = h;
+        } else {
+            reinterpret_cast<float4_t *>(out)[bh * (kHeadDim / 4) + t] = r;
+        }
+    }
 }
 
 // One workgroup of 32 threads per (batch, kv-head): threads 0..15 copy the K token,
@@ -79,10 +95,10 @@ hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B,
 {
     const dim3 grid((uint32_t)((int64_t)B * Hq));
     if (out_f16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(128), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_lse,
                            num_splits, out);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(128), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_lse,
                            num_splits, out);
     return hipGetLastError();
 }

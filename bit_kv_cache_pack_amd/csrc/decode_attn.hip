@@ -12,6 +12,11 @@
 //  * one workgroup = (batch, kv-head, split, head chunk of <= 4 query heads), 4 waves;
 //    each wave streams 32-token tiles of the split (round robin) and keeps its own
 //    online-softmax state; the waves are merged through LDS at the end.
+//  * tiles reach LDS by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) into a
+//    2-slot ring per wave: a wave asks for its next two tiles up front and for tile k+2
+//    as soon as tile k is consumed, so ~10 KB per wave (120 KB per CU at three resident
+//    workgroups) is in flight without holding it in VGPRs; the wave waits on vmcnt for
+//    exactly the tile it is about to use.
 //  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the raw integer codes (exact in fp16,
 //    made with the fp16 magic-number trick) and rows i = 4*head + group of A holding the
 //    query restricted to one 32-channel group. Lane (token n, r) loads group r of token n
@@ -37,12 +42,15 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
+constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer access, gfx9 family
 
 struct DecArgs {
     const uint16_t *q;
+    int32_t q_bytes;             // bytes of q, the range its buffer resource covers
     int32_t Hq, Hkv, gq, head_base;
     const uint8_t *kp, *vp;
     int64_t row_stride;
+    int32_t row_bytes;           // bytes of a packed row the kernel may touch
     int32_t n_packed;
     const uint16_t *kres, *vres;
     int32_t res_cap, n_res;
@@ -52,13 +60,20 @@ struct DecArgs {
     int32_t block_bytes, sz_off;
 };
 
+constexpr int kRing = 2;
+
+// LDS of one workgroup, ~48 KB at 4 bits, so that three workgroups (12 waves) share a CU.
+// A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
+template <int TILE_BYTES>
 struct Smem {
-    float p[kWaves][4][kTile];   // p of head h, token t of the current tile
-    float sv[kWaves][4][kTile];  // V scale of group g, token t
-    float qs[4][4];              // sum of q over group g, head h
-    float mo[kWaves][4][kHeadDim];
-    float ml[kWaves][4][2];
+    alignas(16) uint8_t ring[kWaves][kRing][TILE_BYTES];   // per-wave ring of staged tiles
+    alignas(16) uint16_t q[kWaves][4][kHeadDim];            // per-wave copy of the chunk's q
+    alignas(16) float p[kWaves][4][kTile];    // p of head h, token t of the current tile
+    alignas(16) float sv[kWaves][4][kTile];   // V scale of group g, token t
+    alignas(16) float ml[kWaves][4][2];
+    __device__ __forceinline__ float *mo(int w) { return reinterpret_cast<float *>(&ring[w][0][0]); }
 };
+static_assert(kRing * 1024 * 3 >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
 
 __device__ __forceinline__ void lds_fence()
 {
@@ -76,108 +91,212 @@ __device__ __forceinline__ half8_t perm_octet_f16(u32x4 w)
     return half8_t{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
-template <int BITS>
-struct KGroup;   // one token's 32-channel group of K codes
+typedef __attribute__((address_space(3))) void lds_void;
 
+// Tile geometry in LDS: K codes | V codes | K scale/zero | V scale/zero, each in the
+// order the packed block stores them (32 tokens).
+template <int BITS>
+struct TileGeom {
+    static constexpr int TOKB = kHeadDim * BITS / 8;   // code bytes per token
+    static constexpr int GB = 4 * BITS;                // code bytes per group
+    static constexpr int CB = kTile * TOKB;            // code bytes per tile (2048/1536/1024)
+    static constexpr int KSZ = 2 * CB;                 // offset of K scale/zero (512 B)
+    static constexpr int VSZ = 2 * CB + 512;           // offset of V scale/zero (512 B)
+    static constexpr int BYTES = 2 * CB + 1024;
+    static constexpr int NI = (BITS == 2 ? 2 : 4) + 2; // direct-to-LDS loads per tile
+};
+__device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint32_t voff, int size)
+{
+    // 16 bytes per lane; lane i's bytes land at lds + 16 * i (lds is wave-uniform)
+    (void)size;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
+}
+
+// Ask for packed tile `tile` (32 tokens) of this row: K and V codes and scale/zero.
+template <int BITS>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           uint8_t *slot, int tile, int lane, int block_bytes,
+                                           int sz_off)
+{
+    using G = TileGeom<BITS>;
+    const int tok0 = tile * kTile;
+    const uint32_t blk = (uint32_t)(tok0 >> 7) * (uint32_t)block_bytes;
+    const int tb0 = tok0 & 127;
+    const uint32_t c0 = blk + tb0 * G::TOKB;
+    if (BITS == 3) {          // 1536 B = 64 lanes x 16 B + 32 lanes x 16 B
+        dma(rk, slot, c0 + lane * 16, 16);
+        dma(rv, slot + G::CB, c0 + lane * 16, 16);
+        if (lane < 32) {
+            dma(rk, slot + 1024, c0 + 1024 + lane * 16, 16);
+            dma(rv, slot + G::CB + 1024, c0 + 1024 + lane * 16, 16);
+        }
+    } else {
+#pragma unroll
+        for (int k = 0; k < G::CB / 1024; ++k) {
+            dma(rk, slot + 1024 * k, c0 + 1024 * k + lane * 16, 16);
+            dma(rv, slot + G::CB + 1024 * k, c0 + 1024 * k + lane * 16, 16);
+        }
+    }
+    if (lane < 32) {          // 32 tokens x 16 B of scale/zero each for K and V
+        const uint32_t s0 = blk + sz_off + tb0 * 16 + lane * 16;
+        dma(rk, slot + G::KSZ, s0, 16);
+        dma(rv, slot + G::VSZ, s0, 16);
+    }
+}
+
+// s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// wait until tile k is in LDS, when `after` (< kRing) younger tiles may still be in flight
+template <int BITS>
+__device__ __forceinline__ void wait_tile(int after)
+{
+    constexpr int NI = TileGeom<BITS>::NI;
+    static_assert(kRing == 2, "one younger tile at most");
+    if (after >= 1) wait_vm<NI>();
+    else wait_vm<0>();
+}
+
+// wait for the q copy, requested before `tiles` (0..kRing) tiles
+template <int BITS>
+__device__ __forceinline__ void wait_q(int tiles)
+{
+    constexpr int NI = TileGeom<BITS>::NI;
+    if (tiles >= 2) wait_vm<2 * NI>();
+    else if (tiles == 1) wait_vm<NI>();
+    else wait_vm<0>();
+}
+
+// K codes of token t (0..31 in the tile), group r, as channel octets
+template <int BITS>
+struct KGroup;
 template <>
 struct KGroup<4> {
     u32x4 w;
-    __device__ __forceinline__ void load(const uint8_t *p) { w = *reinterpret_cast<const u32x4 *>(p); }
-    __device__ __forceinline__ half8_t octet(int o) const { return unpack_octet4(w[o]); }
+    __device__ __forceinline__ void load(const uint8_t *slot, int t, int r)
+    {
+        w = *reinterpret_cast<const u32x4 *>(slot + t * 64 + r * 16);
+    }
+    __device__ __forceinline__ half8_t octet(int o, const Magic &M) const { return unpack_octet4(w[o], M); }
 };
 template <>
 struct KGroup<2> {
     u32x2 w;
-    __device__ __forceinline__ void load(const uint8_t *p) { w = *reinterpret_cast<const u32x2 *>(p); }
-    __device__ __forceinline__ half8_t octet(int o) const
+    __device__ __forceinline__ void load(const uint8_t *slot, int t, int r)
     {
-        return unpack_octet2((o & 1) ? (w[o >> 1] >> 16) : w[o >> 1]);
+        w = *reinterpret_cast<const u32x2 *>(slot + t * 32 + r * 8);
+    }
+    __device__ __forceinline__ half8_t octet(int o, const Magic &M) const
+    {
+        return unpack_octet2((o & 1) ? (w[o >> 1] >> 16) : w[o >> 1], M);
     }
 };
 template <>
 struct KGroup<3> {
     uint32_t w0, w1, w2;
-    __device__ __forceinline__ void load(const uint8_t *p)
+    __device__ __forceinline__ void load(const uint8_t *slot, int t, int r)
     {
-        const uint32_t *d = reinterpret_cast<const uint32_t *>(p);
+        const uint32_t *d = reinterpret_cast<const uint32_t *>(slot + t * 48 + r * 12);
         w0 = d[0];
         w1 = d[1];
         w2 = d[2];
     }
-    __device__ __forceinline__ half8_t octet(int o) const
+    __device__ __forceinline__ half8_t octet(int o, const Magic &M) const
     {
-        uint32_t x = o == 0 ? w0 : o == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
-                               : o == 2 ? __builtin_amdgcn_alignbit(w2, w1, 16) : (w2 >> 8);
-        return unpack_octet3(x);
+        const uint32_t x = o == 0 ? w0 : o == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
+                                     : o == 2 ? __builtin_amdgcn_alignbit(w2, w1, 16) : (w2 >> 8);
+        return unpack_octet3(x, M);
     }
 };
 
-// V codes of channel octet j of one token (low bits of the result)
+// V codes of channel octet j of token t of the tile (low bits of the result)
 template <int BITS>
-__device__ __forceinline__ uint32_t load_v_octet(const uint8_t *tok_row, int j)
+__device__ __forceinline__ uint32_t v_octet(const uint8_t *vcodes, int t, int j)
 {
-    if (BITS == 4) return reinterpret_cast<const uint32_t *>(tok_row)[j];
-    if (BITS == 2) return reinterpret_cast<const uint16_t *>(tok_row)[j];
-    // 3 bits: bytes 3j..3j+2 of the 48-byte row; read the two dwords that cover them.
-    // For j = 15 the second dword is the next 4 bytes of the block (next token's codes,
-    // or the first scale/zero bytes after token 127), always inside the block.
-    const int byte = 3 * j;
-    const uint32_t *d = reinterpret_cast<const uint32_t *>(tok_row + (byte & ~3));
-    return __builtin_amdgcn_alignbit(d[1], d[0], (byte & 3) * 8);
+    if (BITS == 4) return reinterpret_cast<const uint32_t *>(vcodes + t * 64)[j];
+    if (BITS == 2) return reinterpret_cast<const uint16_t *>(vcodes + t * 32)[j];
+    // 3 bits: bytes 3j..3j+2 of the 48-byte row, from the two dwords that cover them
+    // (for t = 31, j = 15 the second dword is the first of the K scale/zero region, in
+    // the same slot)
+    const uint32_t byte = 3 * j;
+    const uint32_t *d = reinterpret_cast<const uint32_t *>(vcodes + t * 48 + (byte & ~3u));
+    return __builtin_amdgcn_alignbit(d[1], d[0], (byte & 3u) * 8);
 }
 
 template <int BITS>
-__device__ __forceinline__ void pair_tokens(uint32_t a, uint32_t b, half2_t out[8])
+__device__ __forceinline__ void pair_tokens(uint32_t a, uint32_t b, const Magic &M, half2_t out[8])
 {
-    if (BITS == 4) pair_tokens4(a, b, out);
-    else if (BITS == 2) pair_tokens2(a, b, out);
-    else pair_tokens3(a, b, out);
+    if (BITS == 4) pair_tokens4(a, b, M, out);
+    else if (BITS == 2) pair_tokens2(a, b, M, out);
+    else pair_tokens3(a, b, M, out);
 }
 
-__device__ __forceinline__ float sel4(const float4_t &v, int k)
+// v[k] for a lane-varying k in 0..3, as two levels of selects (a runtime vector index
+// would otherwise go through scratch memory)
+__device__ __forceinline__ float sel4(float4_t v, int k)
 {
-    return k == 0 ? v[0] : k == 1 ? v[1] : k == 2 ? v[2] : v[3];
+    const float a = (k & 1) ? v[1] : v[0];
+    const float b = (k & 1) ? v[3] : v[2];
+    return (k & 2) ? b : a;
+}
+__device__ __forceinline__ uint32_t sel4u(u32x4 v, int k)
+{
+    const uint32_t a = (k & 1) ? v[1] : v[0];
+    const uint32_t b = (k & 1) ? v[3] : v[2];
+    return (k & 2) ? b : a;
 }
 
-// Softmax update and PV for one 32-token tile whose logits (exp2 domain) are lg[0]
-// (token n) and lg[1] (token 16 + n), the V B-operand pairs vpair[m][c] (tokens 8r+2m,
-// 8r+2m+1 of the tile, channel c of octet n), and the per-token V scale of group r
-// already written to LDS by this lane.
-template <int NH>
-__device__ __forceinline__ void softmax_pv(Smem &sm, int wave, int n, int r, const float lg[2],
+// Online-softmax state of one wave: lane (n, r) tracks head r.
+struct WaveState {
+    float m, l;
+    float zacc[4];     // sum_t p_t * zero'_v(t, g) for head r, group g (lane partial)
+    float4_t dpv[8];   // PV accumulators: rows 4h+g, column n <-> channel 8n + c
+};
+
+// Softmax update and PV for one 32-token tile. lg[u]: logits (exp2 domain) of token
+// 16u + n for head r; zv[u][g]: V zero-point term of that token; vpair[m][c]: the V
+// operand pair (tokens 8r+2m, 8r+2m+1; channel 8n + c). The V scale of (token, group r)
+// is already in sm.sv.
+template <int NH, class SM>
+__device__ __forceinline__ void softmax_pv(SM &sm, int wave, int n, int r, const float lg[2],
                                            const float zv[2][4], const half2_t vpair[4][8],
-                                           float &m, float &l, float zacc[4], float4_t dpv[8])
+                                           WaveState &st)
 {
-    float tmax = row_max16(fmaxf(lg[0], lg[1]));
-    const float mnew = fmaxf(m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+    const float tmax = row_max16(fmaxf(lg[0], lg[1]));
+    const float mnew = fmaxf(st.m, tmax);
+    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
     const float p0 = __builtin_amdgcn_exp2f(lg[0] - mnew);
     const float p1 = __builtin_amdgcn_exp2f(lg[1] - mnew);
-    m = mnew;
+    st.m = mnew;
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
-        l *= alpha;
+        st.l *= alpha;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) zacc[g] *= alpha;
+        for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) dpv[c] *= alpha;
+        for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
     }
-    l += p0 + p1;
+    st.l += p0 + p1;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) zacc[g] += p0 * zv[0][g] + p1 * zv[1][g];
+    for (int g = 0; g < 4; ++g) st.zacc[g] = __builtin_fmaf(p1, zv[1][g], __builtin_fmaf(p0, zv[0][g], st.zacc[g]));
 
     sm.p[wave][r][n] = p0;
     sm.p[wave][r][16 + n] = p1;
     lds_fence();
 
     // A operand of PV: lane (i, r) holds rows i = 4h + g, token slots 8r .. 8r+7
-    const int i = n;
-    const int hA = i >> 2, gA = i & 3;
+    const int hA = n >> 2, gA = n & 3;
     const float4_t pl = *reinterpret_cast<const float4_t *>(&sm.p[wave][hA][8 * r]);
     const float4_t ph = *reinterpret_cast<const float4_t *>(&sm.p[wave][hA][8 * r + 4]);
     const float4_t sl = *reinterpret_cast<const float4_t *>(&sm.sv[wave][gA][8 * r]);
     const float4_t sh = *reinterpret_cast<const float4_t *>(&sm.sv[wave][gA][8 * r + 4]);
-    float w[8] = {pl[0] * sl[0], pl[1] * sl[1], pl[2] * sl[2], pl[3] * sl[3],
-                  ph[0] * sh[0], ph[1] * sh[1], ph[2] * sh[2], ph[3] * sh[3]};
+    const float w[8] = {pl[0] * sl[0], pl[1] * sl[1], pl[2] * sl[2], pl[3] * sl[3],
+                        ph[0] * sh[0], ph[1] * sh[1], ph[2] * sh[2], ph[3] * sh[3]};
     half8_t ahi, alo;
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
@@ -190,17 +309,62 @@ __device__ __forceinline__ void softmax_pv(Smem &sm, int wave, int n, int r, con
     for (int c = 0; c < 8; ++c) {
         const half8_t bv{vpair[0][c].x, vpair[0][c].y, vpair[1][c].x, vpair[1][c].y,
                          vpair[2][c].x, vpair[2][c].y, vpair[3][c].x, vpair[3][c].y};
-        dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, dpv[c], 0, 0, 0);
-        dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, dpv[c], 0, 0, 0);
+        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, st.dpv[c], 0, 0, 0);
+        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, st.dpv[c], 0, 0, 0);
     }
     // the next tile rewrites sm.p / sm.sv only after these reads have returned
     lds_fence();
 }
 
+template <int BITS, int NH, class SM>
+__device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const half8_t aq[4],
+                                            const float qs[4], float sm_log2, const Magic &M,
+                                            int wave, int n, int r, WaveState &st)
+{
+    using G = TileGeom<BITS>;
+    KGroup<BITS> kc[2];
+    u32x4 ksz[2], vsz[2];
+    uint32_t vc[8];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        kc[u].load(slot, 16 * u + n, r);
+        ksz[u] = *reinterpret_cast<const u32x4 *>(slot + G::KSZ + (16 * u + n) * 16);
+        vsz[u] = *reinterpret_cast<const u32x4 *>(slot + G::VSZ + (16 * u + n) * 16);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) vc[e] = v_octet<BITS>(slot + G::CB, 8 * r + e, n);
+
+    float lg[2], zv[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int o = 0; o < 4; ++o)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[o], kc[u].octet(o, M), acc, 0, 0, 0);
+        float s = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const half2_t szk = as_h2(ksz[u][g]);
+            s = __builtin_fmaf((float)szk.x, acc[g], s);
+            s = __builtin_fmaf((float)szk.y, qs[g], s);
+            const half2_t szv = as_h2(vsz[u][g]);
+            // the V operand carries codes + 64: zero' = zero - 64 * scale
+            zv[u][g] = __builtin_fmaf(-64.0f, (float)szv.x, (float)szv.y);
+        }
+        lg[u] = s * sm_log2;
+        sm.sv[wave][r][16 * u + n] = (float)as_h2(sel4u(vsz[u], r)).x;
+    }
+    half2_t vpair[4][8];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(vc[2 * mm], vc[2 * mm + 1], M, vpair[mm]);
+    softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, st);
+}
+
 template <int BITS, int NH>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
 {
-    __shared__ Smem sm;
+    using G = TileGeom<BITS>;
+    __shared__ Smem<G::BYTES> sm;
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     const int n = lane & 15;
@@ -224,93 +388,77 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
     }
     with_res = with_res && a.n_res > 0;
 
-    // ---- q: per-group sums (wave 0) and the QK A operands (every wave) ----
-    const uint16_t *qb = a.q + ((int64_t)b * a.Hq + h0) * kHeadDim;
-    if (wave == 0) {
-        const int hh = lane >> 4, gg = (lane >> 2) & 3, qq = lane & 3;
-        float s = 0.0f;
-        if (hh < NH) {
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(qb + hh * kHeadDim + gg * 32 + qq * 8);
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.kp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint8_t *>(a.vp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
+
+    // ---- q of the chunk's heads -> this wave's LDS copy (one 1 KB direct-to-LDS load,
+    // issued before the tile requests so it is the oldest outstanding load) ----
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.q), 0, a.q_bytes, kRsrcWord3);
+    dma(rq, reinterpret_cast<uint8_t *>(&sm.q[wave][0][0]),
+        (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
+
+    // ---- ask for this wave's first tiles ----
+    const int my_lo = tlo + wave;
+    const int nt_w = my_lo < thi ? (thi - my_lo + kWaves - 1) / kWaves : 0;
+    uint8_t *ring = &sm.ring[wave][0][0];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const half2_t hv = as_h2(v[k]);
-                s += (float)hv.x + (float)hv.y;
-            }
-        }
-        s += dpp_f<0xB1>(s);
-        s += dpp_f<0x4E>(s);
-        if (qq == 0) sm.qs[hh][gg] = s;
-    }
+    for (int k = 0; k < kRing; ++k)
+        if (k < nt_w) issue_tile<BITS>(rk, rv, ring + k * G::BYTES, my_lo + k * kWaves, lane,
+                                       a.block_bytes, a.sz_off);
+    wait_q<BITS>(nt_w < kRing ? nt_w : kRing);
+
+    // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
     half8_t aq[4];
     {
         const int hA = n >> 2, gA = n & 3;
         const bool live = (gA == r) && (hA < NH);
 #pragma unroll
         for (int o = 0; o < 4; ++o) {
-            half8_t v = {};
-            if (live) v = perm_octet_f16(*reinterpret_cast<const u32x4 *>(qb + hA * kHeadDim + 32 * r + 8 * o));
-            aq[o] = v;
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hA][32 * r + 8 * o]);
+            aq[o] = live ? perm_octet_f16(w) : half8_t{};
         }
     }
-    __syncthreads();
     float qs[4];
+    {
+        // lane (hh, gg, qq) sums 8 channels; the quad sum is Qs[hh][gg]; lane (n, r) then
+        // fetches Qs[r][g] from lane 16r + 4g
+        const int hh = lane >> 4, gg = (lane >> 2) & 3, qq = lane & 3;
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hh][gg * 32 + qq * 8]);
+        float s = 0.0f;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) qs[g] = sm.qs[r][g];
-
-    float m = -INFINITY, l = 0.0f;
-    float zacc[4] = {0.f, 0.f, 0.f, 0.f};
-    float4_t dpv[8];
-#pragma unroll
-    for (int c = 0; c < 8; ++c) dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
-
-    const uint8_t *krow = a.kp + row * a.row_stride;
-    const uint8_t *vrow = a.vp + row * a.row_stride;
-    constexpr int TOKB = kHeadDim * BITS / 8;       // code bytes per token
-    constexpr int GB = 4 * BITS;                    // code bytes per group
-
-    // ---- packed tiles ----
-    for (int t = tlo + wave; t < thi; t += kWaves) {
-        const int tok0 = t * kTile;
-        const uint8_t *kb = krow + (int64_t)(tok0 >> 7) * a.block_bytes;
-        const uint8_t *vb = vrow + (int64_t)(tok0 >> 7) * a.block_bytes;
-        const int tb0 = tok0 & 127;
-
-        KGroup<BITS> kc[2];
-        u32x4 ksz[2], vsz[2];
-        uint32_t vc[8];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int tb = tb0 + 16 * u + n;
-            kc[u].load(kb + tb * TOKB + r * GB);
-            ksz[u] = *reinterpret_cast<const u32x4 *>(kb + a.sz_off + tb * 16);
-            vsz[u] = *reinterpret_cast<const u32x4 *>(vb + a.sz_off + tb * 16);
+        for (int k = 0; k < 4; ++k) {
+            const half2_t hv = as_h2(v[k]);
+            s += (float)hv.x + (float)hv.y;
         }
+        s = hh < NH ? s : 0.0f;
+        s += dpp_f<0xB1>(s);
+        s += dpp_f<0x4E>(s);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) vc[e] = load_v_octet<BITS>(vb + (tb0 + 8 * r + e) * TOKB, n);
+        for (int g = 0; g < 4; ++g)
+            qs[g] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * r + 4 * g) * 4, __float_as_int(s)));
+    }
 
-        float lg[2], zv[2][4];
+    const Magic M;
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < 4; ++g) st.zacc[g] = 0.0f;
 #pragma unroll
-            for (int o = 0; o < 4; ++o)
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[o], kc[u].octet(o), acc, 0, 0, 0);
-            float s = 0.0f;
-#pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const half2_t szk = as_h2(ksz[u][g]);
-                s = __builtin_fmaf((float)szk.x, acc[g], s);
-                s = __builtin_fmaf((float)szk.y, qs[g], s);
-                const half2_t szv = as_h2(vsz[u][g]);
-                zv[u][g] = (float)szv.y;
-            }
-            lg[u] = s * a.sm_log2;
-            sm.sv[wave][r][16 * u + n] = (float)as_h2(vsz[u][r]).x;
-        }
-        half2_t vpair[4][8];
-#pragma unroll
-        for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(vc[2 * mm], vc[2 * mm + 1], vpair[mm]);
-        softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, m, l, zacc, dpv);
+    for (int c = 0; c < 8; ++c) st.dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+
+    // ---- packed tiles through the ring ----
+    for (int k = 0; k < nt_w; ++k) {
+        const int left = nt_w - 1 - k;                  // younger tiles possibly in flight
+        wait_tile<BITS>(left < kRing - 1 ? left : kRing - 1);
+        uint8_t *slot = ring + (k % kRing) * G::BYTES;
+        packed_tile<BITS, NH>(sm, slot, aq, qs, a.sm_log2, M, wave, n, r, st);
+        wait_lgkm0();                                    // the slot has been read
+        if (k + kRing < nt_w)
+            issue_tile<BITS>(rk, rv, slot, my_lo + (k + kRing) * kWaves, lane, a.block_bytes, a.sz_off);
     }
 
     // ---- residual / sink tokens (fp16), in 32-token tiles ----
@@ -350,28 +498,29 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 for (int c = 0; c < 8; ++c)
                     vpair[mm][c] = as_h2((c & 1) ? pack_hi16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1])
                                                  : pack_lo16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1]));
-            softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, m, l, zacc, dpv);
+            softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, st);
         }
     }
 
     // ---- merge the waves ----
-    const float lsum = row_sum16(l);
+    const float lsum = row_sum16(st.l);
     float zr[4];
 #pragma unroll
-    for (int g = 0; g < 4; ++g) zr[g] = row_sum16(zacc[g]);
+    for (int g = 0; g < 4; ++g) zr[g] = row_sum16(st.zacc[g]);
     {
         const int gj = n >> 2;   // group of channels 8n .. 8n+7
         const float zg = sel4(float4_t{zr[0], zr[1], zr[2], zr[3]}, gj);
         float4_t o0, o1;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-            o0[c] = sel4(dpv[c], gj) + zg;
-            o1[c] = sel4(dpv[4 + c], gj) + zg;
+            o0[c] = sel4(st.dpv[c], gj) + zg;
+            o1[c] = sel4(st.dpv[4 + c], gj) + zg;
         }
-        *reinterpret_cast<float4_t *>(&sm.mo[wave][r][8 * n]) = o0;
-        *reinterpret_cast<float4_t *>(&sm.mo[wave][r][8 * n + 4]) = o1;
+        float *mo = sm.mo(wave) + r * kHeadDim;
+        *reinterpret_cast<float4_t *>(mo + 8 * n) = o0;
+        *reinterpret_cast<float4_t *>(mo + 8 * n + 4) = o1;
         if (n == 0) {
-            sm.ml[wave][r][0] = m;
+            sm.ml[wave][r][0] = st.m;
             sm.ml[wave][r][1] = lsum;
         }
     }
@@ -380,17 +529,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
         const int h = threadIdx.x >> 6;       // 4 heads x 64 threads x 2 channels
         const int d = (threadIdx.x & 63) * 2;
         if (h < NH) {
-            float M = -INFINITY;
+            float Mx = -INFINITY;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.ml[w][h][0]);
+            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.ml[w][h][0]);
             float o0 = 0.f, o1 = 0.f, L = 0.f;
-            if (M != -INFINITY) {
+            if (Mx != -INFINITY) {
 #pragma unroll
                 for (int w = 0; w < kWaves; ++w) {
-                    const float e = __builtin_amdgcn_exp2f(sm.ml[w][h][0] - M);
+                    const float e = __builtin_amdgcn_exp2f(sm.ml[w][h][0] - Mx);
                     L += e * sm.ml[w][h][1];
-                    o0 += e * sm.mo[w][h][d];
-                    o1 += e * sm.mo[w][h][d + 1];
+                    o0 += e * sm.mo(w)[h * kHeadDim + d];
+                    o1 += e * sm.mo(w)[h * kHeadDim + d + 1];
                 }
             }
             const int64_t hq = (int64_t)b * a.Hq + h0 + h;
@@ -399,7 +548,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 const float inv = 1.0f / L;
                 a.part_o[ob] = o0 * inv;
                 a.part_o[ob + 1] = o1 * inv;
-                if (d == 0) a.part_lse[hq * a.S + split] = (M + __log2f(L)) * 0.69314718055994531f;
+                if (d == 0) a.part_lse[hq * a.S + split] = (Mx + __log2f(L)) * 0.69314718055994531f;
             } else {
                 a.part_o[ob] = 0.f;
                 a.part_o[ob + 1] = 0.f;
@@ -445,6 +594,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
 {
     DecArgs a{};
     a.q = p.q;
+    a.q_bytes = (int32_t)((int64_t)p.B * p.Hq * kHeadDim * 2);
     a.Hq = p.Hq;
     a.Hkv = p.Hkv;
     a.gq = p.Hq / p.Hkv;
@@ -464,6 +614,7 @@ hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
     a.part_lse = p.part_lse;
     a.block_bytes = p.block_bytes;
     a.sz_off = p.sz_off;
+    a.row_bytes = (int32_t)((int64_t)(p.n_packed / kBlockTokens) * p.block_bytes);
     const int64_t rows = (int64_t)p.B * p.Hkv;
     const int full = a.gq / 4, tail = a.gq % 4;
     hipError_t e = hipSuccess;

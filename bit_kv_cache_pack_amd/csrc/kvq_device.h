@@ -55,95 +55,118 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t lo, uint32_t hi) { return
 __device__ __forceinline__ half2_t as_h2(uint32_t u) { return __builtin_bit_cast(half2_t, u); }
 __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_cast(uint32_t, h); }
 
-// fp16 magic-number conversion of small integer codes: OR-ing a code into the low
-// mantissa bits of a power of two 2^E gives the fp16 value 2^E + code * 2^(E-10+shift);
-// subtracting 2^E (exact) leaves the code. Each pair below holds two codes in the two
-// halves of a 32-bit word.
-__device__ __forceinline__ half2_t magic_pair(uint32_t bits_in_place, uint32_t mask, uint32_t base_bits)
+// A 32-bit constant held in a VGPR. The fp16 magic-number unpack below is
+// (bits & mask) | base with two 32-bit constants; gfx9 VOP3 takes at most one SGPR
+// operand, so keeping `base` in a VGPR lets the compiler fuse it into one v_and_or_b32.
+__device__ __forceinline__ uint32_t vconst(uint32_t c)
 {
-    const uint32_t u = (bits_in_place & mask) | base_bits;
-    const _Float16 base = __builtin_bit_cast(_Float16, (uint16_t)(base_bits & 0xffff));
-    return as_h2(u) - half2_t{base, base};
+    uint32_t v;
+    asm("v_mov_b32 %0, %1" : "=v"(v) : "n"(c));
+    return v;
 }
 
-// Eight codes of one 8-channel octet -> half8 in the slot order (0,4,1,5,2,6,3,7):
-// slot 2m holds channel m, slot 2m+1 holds channel m+4.
+// fp16 magic-number conversion of small integer codes: OR-ing a code into the mantissa of
+// 2^E, at the bit whose weight is 1, gives the fp16 value 2^E + code exactly.
+//   base 0x6400 = 2^10 (code at bit 0), 0x5C00 = 2^8 (bit 2), 0x5800 = 2^7 (bit 3),
+//   0x5400 = 2^6 (bit 4), 0x4C00 = 2^4 (bit 6).
+struct Magic {
+    uint32_t b10, b8, b7, b6, b4;
+    __device__ __forceinline__ Magic()
+        : b10(vconst(0x64006400u)), b8(vconst(0x5C005C00u)), b7(vconst(0x58005800u)),
+          b6(vconst(0x54005400u)), b4(vconst(0x4C004C00u)) {}
+};
+
+// two codes (one per 16-bit half) -> half2 of 2^E + code
+__device__ __forceinline__ uint32_t mpair(uint32_t bits, uint32_t mask, uint32_t vbase)
+{
+    return (bits & mask) | vbase;
+}
+// ... minus 2^E, exact: the codes themselves
+__device__ __forceinline__ half2_t mexact(uint32_t bits, uint32_t mask, uint32_t vbase, _Float16 e)
+{
+    return as_h2(mpair(bits, mask, vbase)) - half2_t{e, e};
+}
+
+// Eight codes of one 8-channel octet -> exact half8 in the slot order (0,4,1,5,2,6,3,7):
+// slot 2m holds channel m, slot 2m+1 holds channel m+4 (used for K, where the query
+// operand is laid out in the same order).
 //  4-bit: the octet is a 32-bit word, code i at bits 4i.
-__device__ __forceinline__ half8_t unpack_octet4(uint32_t w)
+__device__ __forceinline__ half8_t unpack_octet4(uint32_t w, const Magic &M)
 {
     const uint32_t w8 = w >> 8;
-    half2_t p0 = magic_pair(w, 0x000F000Fu, 0x64006400u);   // c0,c4   (2^10 + c)
-    half2_t p1 = magic_pair(w, 0x00F000F0u, 0x54005400u);   // c1,c5   (2^6 + c)
-    half2_t p2 = magic_pair(w8, 0x000F000Fu, 0x64006400u);  // c2,c6
-    half2_t p3 = magic_pair(w8, 0x00F000F0u, 0x54005400u);  // c3,c7
+    const half2_t p0 = mexact(w, 0x000F000Fu, M.b10, (_Float16)1024.f);  // c0,c4
+    const half2_t p1 = mexact(w, 0x00F000F0u, M.b6, (_Float16)64.f);     // c1,c5
+    const half2_t p2 = mexact(w8, 0x000F000Fu, M.b10, (_Float16)1024.f); // c2,c6
+    const half2_t p3 = mexact(w8, 0x00F000F0u, M.b6, (_Float16)64.f);    // c3,c7
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 //  2-bit: the octet is 16 bits (low half of y), code i at bits 2i.
-__device__ __forceinline__ half8_t unpack_octet2(uint32_t y)
+__device__ __forceinline__ half8_t unpack_octet2(uint32_t y, const Magic &M)
 {
     // c0..c3 (byte 0) stay in bits 0-7; c4..c7 (byte 1) move to bits 16-23
     const uint32_t w = perm_b32(0u, y, 0x0c010c00u);
-    half2_t p0 = magic_pair(w, 0x00030003u, 0x64006400u);   // 2^10 + c
-    half2_t p1 = magic_pair(w, 0x000C000Cu, 0x5C005C00u);   // 2^8 + c
-    half2_t p2 = magic_pair(w, 0x00300030u, 0x54005400u);   // 2^6 + c
-    half2_t p3 = magic_pair(w, 0x00C000C0u, 0x4C004C00u);   // 2^4 + c
+    const half2_t p0 = mexact(w, 0x00030003u, M.b10, (_Float16)1024.f);
+    const half2_t p1 = mexact(w, 0x000C000Cu, M.b8, (_Float16)256.f);
+    const half2_t p2 = mexact(w, 0x00300030u, M.b6, (_Float16)64.f);
+    const half2_t p3 = mexact(w, 0x00C000C0u, M.b4, (_Float16)16.f);
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 //  3-bit: the octet is 24 bits (low bits of x), code i at bits 3i.
-__device__ __forceinline__ half8_t unpack_octet3(uint32_t x)
+__device__ __forceinline__ half8_t unpack_octet3(uint32_t x, const Magic &M)
 {
     // c0..c3 (bits 0-11) stay; c4..c7 (bits 12-23) move to bits 16-27
-    const uint32_t w = __builtin_amdgcn_ubfe(x, 0, 12) | ((x << 4) & 0x0FFF0000u);
-    half2_t p0 = magic_pair(w, 0x00070007u, 0x64006400u);        // 2^10 + c
-    half2_t p1 = magic_pair(w, 0x00380038u, 0x58005800u);        // 2^7 + c
-    half2_t p2 = magic_pair(w, 0x01C001C0u, 0x4C004C00u);        // 2^4 + c
-    half2_t p3 = magic_pair(w >> 3, 0x01C001C0u, 0x4C004C00u);   // 2^4 + c
+    const uint32_t w = pack_lo16(x, x >> 12);
+    const half2_t p0 = mexact(w, 0x00070007u, M.b10, (_Float16)1024.f);
+    const half2_t p1 = mexact(w, 0x00380038u, M.b7, (_Float16)128.f);
+    const half2_t p2 = mexact(w, 0x01C001C0u, M.b4, (_Float16)16.f);
+    const half2_t p3 = mexact(w >> 3, 0x01C001C0u, M.b4, (_Float16)16.f);
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 
 // Two tokens' octets (a = token 2m, b = token 2m+1) -> for each channel c of the octet a
-// half2 {code(a, c), code(b, c)}; out[c] for c = 0..7.
-__device__ __forceinline__ void pair_tokens4(uint32_t a, uint32_t b, half2_t out[8])
+// half2 {64 + code(a, c), 64 + code(b, c)} (V operand; the 64 offset is removed through
+// the zero-point term: zero' = zero - 64 * scale). Every code is first moved to the bit
+// whose weight at 2^6 is 1 (bits 4.. of each half).
+__device__ __forceinline__ void pair_tokens4(uint32_t a, uint32_t b, const Magic &M, half2_t out[8])
 {
     const uint32_t lo = pack_lo16(a, b);   // channels 0..3 of both tokens
     const uint32_t hi = pack_hi16(a, b);   // channels 4..7
-    const uint32_t lo8 = lo >> 8, hi8 = hi >> 8;
-    out[0] = magic_pair(lo, 0x000F000Fu, 0x64006400u);
-    out[1] = magic_pair(lo, 0x00F000F0u, 0x54005400u);
-    out[2] = magic_pair(lo8, 0x000F000Fu, 0x64006400u);
-    out[3] = magic_pair(lo8, 0x00F000F0u, 0x54005400u);
-    out[4] = magic_pair(hi, 0x000F000Fu, 0x64006400u);
-    out[5] = magic_pair(hi, 0x00F000F0u, 0x54005400u);
-    out[6] = magic_pair(hi8, 0x000F000Fu, 0x64006400u);
-    out[7] = magic_pair(hi8, 0x00F000F0u, 0x54005400u);
+    const uint32_t m = 0x00F000F0u;
+    out[0] = as_h2(mpair(lo << 4, m, M.b6));
+    out[1] = as_h2(mpair(lo, m, M.b6));
+    out[2] = as_h2(mpair(lo >> 4, m, M.b6));
+    out[3] = as_h2(mpair(lo >> 8, m, M.b6));
+    out[4] = as_h2(mpair(hi << 4, m, M.b6));
+    out[5] = as_h2(mpair(hi, m, M.b6));
+    out[6] = as_h2(mpair(hi >> 4, m, M.b6));
+    out[7] = as_h2(mpair(hi >> 8, m, M.b6));
 }
-__device__ __forceinline__ void pair_tokens2(uint32_t a, uint32_t b, half2_t out[8])
+__device__ __forceinline__ void pair_tokens2(uint32_t a, uint32_t b, const Magic &M, half2_t out[8])
 {
     const uint32_t u = pack_lo16(a, b);    // 16-bit octets side by side
-    const uint32_t u8 = u >> 8;
-    out[0] = magic_pair(u, 0x00030003u, 0x64006400u);
-    out[1] = magic_pair(u, 0x000C000Cu, 0x5C005C00u);
-    out[2] = magic_pair(u, 0x00300030u, 0x54005400u);
-    out[3] = magic_pair(u, 0x00C000C0u, 0x4C004C00u);
-    out[4] = magic_pair(u8, 0x00030003u, 0x64006400u);
-    out[5] = magic_pair(u8, 0x000C000Cu, 0x5C005C00u);
-    out[6] = magic_pair(u8, 0x00300030u, 0x54005400u);
-    out[7] = magic_pair(u8, 0x00C000C0u, 0x4C004C00u);
+    const uint32_t m = 0x00300030u;
+    out[0] = as_h2(mpair(u << 4, m, M.b6));
+    out[1] = as_h2(mpair(u << 2, m, M.b6));
+    out[2] = as_h2(mpair(u, m, M.b6));
+    out[3] = as_h2(mpair(u >> 2, m, M.b6));
+    out[4] = as_h2(mpair(u >> 4, m, M.b6));
+    out[5] = as_h2(mpair(u >> 6, m, M.b6));
+    out[6] = as_h2(mpair(u >> 8, m, M.b6));
+    out[7] = as_h2(mpair(u >> 10, m, M.b6));
 }
-__device__ __forceinline__ void pair_tokens3(uint32_t a, uint32_t b, half2_t out[8])
+__device__ __forceinline__ void pair_tokens3(uint32_t a, uint32_t b, const Magic &M, half2_t out[8])
 {
-    // channels 0..3 (bits 0-11) of a in the low half, of b in the high half
-    const uint32_t lo = (a & 0x0000FFFFu) | (b << 16);
-    // channels 4..7 (bits 12-23)
-    const uint32_t hi = ((a >> 12) & 0x0000FFFFu) | ((b << 4) & 0xFFFF0000u);
-    out[0] = magic_pair(lo, 0x00070007u, 0x64006400u);
-    out[1] = magic_pair(lo, 0x00380038u, 0x58005800u);
-    out[2] = magic_pair(lo, 0x01C001C0u, 0x4C004C00u);
-    out[3] = magic_pair(lo >> 3, 0x01C001C0u, 0x4C004C00u);
-    out[4] = magic_pair(hi, 0x00070007u, 0x64006400u);
-    out[5] = magic_pair(hi, 0x00380038u, 0x58005800u);
-    out[6] = magic_pair(hi, 0x01C001C0u, 0x4C004C00u);
-    out[7] = magic_pair(hi >> 3, 0x01C001C0u, 0x4C004C00u);
+    const uint32_t lo = pack_lo16(a, b);              // channels 0..3 (bits 0-11 of each)
+    const uint32_t hi = pack_lo16(a >> 12, b >> 12);  // channels 4..7
+    const uint32_t m = 0x00700070u;
+    out[0] = as_h2(mpair(lo << 4, m, M.b6));
+    out[1] = as_h2(mpair(lo << 1, m, M.b6));
+    out[2] = as_h2(mpair(lo >> 2, m, M.b6));
+    out[3] = as_h2(mpair(lo >> 5, m, M.b6));
+    out[4] = as_h2(mpair(hi << 4, m, M.b6));
+    out[5] = as_h2(mpair(hi << 1, m, M.b6));
+    out[6] = as_h2(mpair(hi >> 2, m, M.b6));
+    out[7] = as_h2(mpair(hi >> 5, m, M.b6));
 }
 
 }  // namespace kvq

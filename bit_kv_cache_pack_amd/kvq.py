@@ -163,7 +163,7 @@ def kvq_append_residual(k_new, v_new, k_res, v_res, B: int, Hkv: int, head_dim: 
 def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
     """Same rule as the header's kvq_suggest_splits."""
     rows = B * Hkv
-    tiles = n_tokens // 32 + 1
-    want = (4 * cu_count + rows - 1) // rows
-    cap = tiles // 4 + 1
+    tiles = n_tokens // 32
+    want = (3 * cu_count + rows - 1) // rows
+    cap = tiles // 8
     return int(max(1, min(256, min(want, cap))))

@@ -129,15 +129,16 @@ static inline int64_t kvq_block_bytes(const kvq_format *f)
 {
     return kvq_align64(kvq_flag_offset(f) + kvq_flag_bytes(f));
 }
-/* A split count that gives a few thousand workgroups' worth of tiles on `cu_count` CUs:
-   enough splits that B*Hkv*S fills the chip several times, none with fewer than 4 tiles. */
+/* A split count for decode on `cu_count` CUs: enough splits that B*Hkv*S workgroups give
+   about three resident workgroups per CU (the decode kernel's LDS use allows three), but no
+   fewer than 8 packed 32-token tiles per split. */
 static inline int32_t kvq_suggest_splits(int32_t B, int32_t Hkv, int32_t n_tokens,
                                          int32_t cu_count)
 {
     int64_t rows = (int64_t)B * Hkv;
-    int64_t tiles = n_tokens / 32 + 1;
-    int64_t want = (4LL * cu_count + rows - 1) / rows;     /* ~4 workgroups per CU */
-    int64_t cap = tiles / 4 + 1;
+    int64_t tiles = n_tokens / 32;
+    int64_t want = (3LL * cu_count + rows - 1) / rows;
+    int64_t cap = tiles / 8;
     int64_t s = want < cap ? want : cap;
     if (s < 1) s = 1;
     if (s > 256) s = 256;

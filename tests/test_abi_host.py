@@ -148,4 +148,4 @@ def test_suggest_splits_bounds():
                       (1, 1, 1)]:
         s = K.suggest_splits(B, Hkv, n)
         assert 1 <= s <= 256
-        assert s <= n // 32 // 4 + 1
+        assert s <= max(1, n // 32 // 8)
