@@ -151,19 +151,22 @@ def main():
         decode(i)
         K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sptr)
 
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-    # timed region: K whole steps back to back
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
-    t_start.record(stream)
-    for i in range(args.steps):
-        step(i)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
-    ms_per_step = total_ms / args.steps
+
+    def timed(fn, n):
+        for i in range(args.warmup):
+            fn(i)
+        torch.cuda.synchronize()
+        t_start.record(stream)
+        for i in range(n):
+            fn(i)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        return t_start.elapsed_time(t_end) / n
+
+    # timed region: K whole steps back to back
+    ms_per_step = timed(step, args.steps)
     # decode kernel duration: HIP events around every launch, on the launch stream
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]

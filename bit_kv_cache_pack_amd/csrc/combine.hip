@@ -15,51 +15,55 @@ namespace kvq {
 namespace {
 
 // One workgroup of 256 threads per (batch, head). Thread t owns output channels
-// 4*(t % 32) .. +3 for the splits s = t / 32, t / 32 + 8, ...; the eight partial sums of
-// each channel are then added through LDS. All loads of a thread are independent
-// 16-byte reads, so the whole partial block streams in parallel.
+// 4*(t % 32) .. +3 for the splits s = t / 32, t / 32 + 8, ...; it merges them in one pass
+// with its own running maximum (all of its loads can be in flight at once), and the eight
+// per-thread results of each channel are merged through LDS with the same rule.
 template <bool F16>
 __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_lse, int S,
                                                       void *__restrict__ out)
 {
-    __shared__ float red_m[4];
     __shared__ float4_t red_o[8][32];
-    __shared__ float red_w[8];
+    __shared__ float red_m[8], red_w[8];
     const int64_t bh = blockIdx.x;
     const int t = threadIdx.x;
-    const float *lse = part_lse + bh * S;
-
-    float m = -INFINITY;
-    for (int s = t; s < S; s += 256) m = fmaxf(m, lse[s]);
-#pragma unroll
-    for (int k = 32; k >= 1; k >>= 1) m = fmaxf(m, __shfl_xor(m, k));
-    if ((t & 63) == 0) red_m[t >> 6] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_m[0], red_m[1]), fmaxf(red_m[2], red_m[3]));
-
     const int cq = t & 31, sg = t >> 5;
+    const float *lse = part_lse + bh * S;
     const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) + cq;
+
+    float m = -INFINITY, ws = 0.0f;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
-    float wsum = 0.0f;
-#pragma unroll 4
+#pragma unroll 8
     for (int s = sg; s < S; s += 8) {
         const float ls = lse[s];
-        const float w = ls == -INFINITY ? 0.0f : __expf(ls - M);
         const float4_t x = o[(int64_t)s * (kHeadDim / 4)];
+        if (ls > m) {                  // new running maximum: rescale what is accumulated
+            const float c = __expf(m - ls);
+            acc *= c;
+            ws *= c;
+            m = ls;
+        }
+        const float w = ls == -INFINITY ? 0.0f : __expf(ls - m);
         acc += w * x;
-        wsum += w;
+        ws += w;
     }
     red_o[sg][cq] = acc;
-    if (cq == 0) red_w[sg] = wsum;
+    if (cq == 0) {
+        red_m[sg] = m;
+        red_w[sg] = ws;
+    }
     __syncthreads();
     if (t < 32) {
-        float4_t tot = red_o[0][t];
-        float W = red_w[0];
+        float M = red_m[0];
 #pragma unroll
-        for (int k = 1; k < 8; ++k) {
-            tot += red_o[k][t];
-            W += red_w[k];
+        for (int k = 1; k < 8; ++k) M = fmaxf(M, red_m[k]);
+        float4_t tot = {0.f, 0.f, 0.f, 0.f};
+        float W = 0.0f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float c = red_m[k] == -INFINITY ? 0.0f : __expf(red_m[k] - M);
+            tot += c * red_o[k][t];
+            W += c * red_w[k];
         }
         const float4_t r = tot / W;
         if (F16) {

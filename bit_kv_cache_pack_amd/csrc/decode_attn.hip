@@ -42,6 +42,10 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
+// a tile's max may exceed the running max by up to 2^kSlack before the accumulators are
+// rescaled; p * scale_v then stays below 65504 whenever scale_v < 2^(15 - kSlack)
+constexpr float kSlack = 8.0f;
+constexpr float kBigScale = 128.0f;   // 2^(15 - kSlack)
 constexpr uint32_t kRsrcWord3 = 0x00020000u;   // raw buffer access, gfx9 family
 
 struct DecArgs {
@@ -237,6 +241,12 @@ __device__ __forceinline__ void pair_tokens(uint32_t a, uint32_t b, const Magic 
     else pair_tokens3(a, b, M, out);
 }
 
+// PV operand slot order: slot e of lane group r holds tile token 4e + r, so the eight V-code
+// reads of the four lane groups hit adjacent token rows (distinct LDS banks). Per-token
+// values (p, scale_v) are stored at the slot position pos(t) = 8 * (t % 4) + t / 4 so that
+// lane group r reads its eight values as two contiguous 16-byte words.
+__device__ __forceinline__ int slot_pos(int t) { return 8 * (t & 3) + (t >> 2); }
+
 // v[k] for a lane-varying k in 0..3, as two levels of selects (a runtime vector index
 // would otherwise go through scratch memory)
 __device__ __forceinline__ float sel4(float4_t v, int k)
@@ -261,32 +271,36 @@ struct WaveState {
 
 // Softmax update and PV for one 32-token tile. lg[u]: logits (exp2 domain) of token
 // 16u + n for head r; zv[u][g]: V zero-point term of that token; vpair[m][c]: the V
-// operand pair (tokens 8r+2m, 8r+2m+1; channel 8n + c). The V scale of (token, group r)
-// is already in sm.sv.
+// operand pair (slots 2m, 2m+1 of lane group r, i.e. tokens 8m + r and 8m + 4 + r;
+// channel 8n + c). The V scale of (token, group r) is already in sm.sv.
 template <int NH, class SM>
 __device__ __forceinline__ void softmax_pv(SM &sm, int wave, int n, int r, const float lg[2],
                                            const float zv[2][4], const half2_t vpair[4][8],
-                                           WaveState &st)
+                                           bool big_scale, WaveState &st)
 {
+    // Lazy rescale: the reference max m only moves when the tile's max exceeds it by more
+    // than 2^kSlack (log2 units), or exceeds it at all while a V scale is so large that
+    // p * scale could leave the fp16 range of the PV operand; otherwise p <= 2^kSlack.
     const float tmax = row_max16(fmaxf(lg[0], lg[1]));
-    const float mnew = fmaxf(st.m, tmax);
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
-    const float p0 = __builtin_amdgcn_exp2f(lg[0] - mnew);
-    const float p1 = __builtin_amdgcn_exp2f(lg[1] - mnew);
-    st.m = mnew;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f) != 0) {
+    const bool grow = (tmax > st.m + kSlack) || (big_scale && tmax > st.m);
+    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
+        const float mnew = grow ? tmax : st.m;
+        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
+        st.m = mnew;
         st.l *= alpha;
 #pragma unroll
         for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
 #pragma unroll
         for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
     }
+    const float p0 = __builtin_amdgcn_exp2f(lg[0] - st.m);
+    const float p1 = __builtin_amdgcn_exp2f(lg[1] - st.m);
     st.l += p0 + p1;
 #pragma unroll
     for (int g = 0; g < 4; ++g) st.zacc[g] = __builtin_fmaf(p1, zv[1][g], __builtin_fmaf(p0, zv[0][g], st.zacc[g]));
 
-    sm.p[wave][r][n] = p0;
-    sm.p[wave][r][16 + n] = p1;
+    sm.p[wave][r][slot_pos(n)] = p0;
+    sm.p[wave][r][slot_pos(16 + n)] = p1;
     lds_fence();
 
     // A operand of PV: lane (i, r) holds rows i = 4h + g, token slots 8r .. 8r+7
@@ -332,7 +346,7 @@ __device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const h
         vsz[u] = *reinterpret_cast<const u32x4 *>(slot + G::VSZ + (16 * u + n) * 16);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vc[e] = v_octet<BITS>(slot + G::CB, 8 * r + e, n);
+    for (int e = 0; e < 8; ++e) vc[e] = v_octet<BITS>(slot + G::CB, 4 * e + r, n);
 
     float lg[2], zv[2][4];
 #pragma unroll
@@ -352,12 +366,19 @@ __device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const h
             zv[u][g] = __builtin_fmaf(-64.0f, (float)szv.x, (float)szv.y);
         }
         lg[u] = s * sm_log2;
-        sm.sv[wave][r][16 * u + n] = (float)as_h2(sel4u(vsz[u], r)).x;
+        sm.sv[wave][r][slot_pos(16 * u + n)] = (float)as_h2(sel4u(vsz[u], r)).x;
     }
+    // any V scale of the tile at or above 2^(15 - kSlack)? (fp16 compare on the low halves)
+    bool big = false;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) big |= as_h2(vsz[u][g]).x >= (_Float16)kBigScale;
+    const bool big_scale = __builtin_amdgcn_ballot_w64(big) != 0;
     half2_t vpair[4][8];
 #pragma unroll
     for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(vc[2 * mm], vc[2 * mm + 1], M, vpair[mm]);
-    softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, st);
+    softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, big_scale, st);
 }
 
 template <int BITS, int NH>
@@ -482,12 +503,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 lg[u] = ts < a.n_res ? s * a.sm_log2 : -INFINITY;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zv[u][g] = 0.0f;
-                sm.sv[wave][r][16 * u + n] = 1.0f;
+                sm.sv[wave][r][slot_pos(16 * u + n)] = 1.0f;
             }
             u32x4 vt[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int ts = rt * kTile + 8 * r + e;
+                const int ts = rt * kTile + 4 * e + r;
                 const int tc = ts < a.n_res ? ts : a.n_res - 1;
                 vt[e] = *reinterpret_cast<const u32x4 *>(vr + (int64_t)tc * kHeadDim + 8 * n);
             }
@@ -498,7 +519,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 for (int c = 0; c < 8; ++c)
                     vpair[mm][c] = as_h2((c & 1) ? pack_hi16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1])
                                                  : pack_lo16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1]));
-            softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, st);
+            softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, false, st);
         }
     }
 
@@ -544,16 +565,16 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
             }
             const int64_t hq = (int64_t)b * a.Hq + h0 + h;
             const int64_t ob = (hq * a.S + split) * kHeadDim + d;
+            float v0 = 0.f, v1 = 0.f, lse = -INFINITY;
             if (L > 0.f) {
                 const float inv = 1.0f / L;
-                a.part_o[ob] = o0 * inv;
-                a.part_o[ob + 1] = o1 * inv;
-                if (d == 0) a.part_lse[hq * a.S + split] = (Mx + __log2f(L)) * 0.69314718055994531f;
-            } else {
-                a.part_o[ob] = 0.f;
-                a.part_o[ob + 1] = 0.f;
-                if (d == 0) a.part_lse[hq * a.S + split] = -INFINITY;
+                v0 = o0 * inv;
+                v1 = o1 * inv;
+                lse = (Mx + __log2f(L)) * 0.69314718055994531f;
             }
+            a.part_o[ob] = v0;
+            a.part_o[ob + 1] = v1;
+            if (d == 0) a.part_lse[hq * a.S + split] = lse;
         }
     }
 }
@@ -561,8 +582,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
 template <int BITS, int NH>
 hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_kernel<BITS, NH>), dim3((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks),
-                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BITS, NH>),
+                       dim3((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks), dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

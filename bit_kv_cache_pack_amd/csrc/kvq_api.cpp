@@ -53,13 +53,16 @@ kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_
         stream));
 }
 
-kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32_t B,
-                                int32_t Hq, int32_t Hkv, const void *k_packed,
-                                const void *v_packed, int64_t packed_row_stride_bytes,
-                                int32_t n_packed_tokens, const void *k_res_fp16,
-                                const void *v_res_fp16, int32_t res_capacity, int32_t n_res,
-                                float sm_scale, int32_t num_splits, float *part_o,
-                                float *part_lse, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq,
+                         int32_t Hkv, const void *k_packed, const void *v_packed,
+                         int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
+                         const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
+                         int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
+                         float *part_lse, hipStream_t stream)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
@@ -73,11 +76,13 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
     if (num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
     if (!isfinite(sm_scale)) return KVQ_ERR_SHAPE;
     if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if ((int64_t)B * Hq * fmt->head_dim * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
     if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
     const int64_t bb = kvq_block_bytes(fmt);
     if (n_packed_tokens > 0) {
         if (packed_row_stride_bytes % 64 != 0) return KVQ_ERR_ALIGN;
         if (packed_row_stride_bytes < (int64_t)(n_packed_tokens / 128) * bb) return KVQ_ERR_SHAPE;
+        if ((int64_t)(n_packed_tokens / 128) * bb > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
         if (!aligned64(k_packed) || !aligned64(v_packed)) return KVQ_ERR_ALIGN;
     }
     if (n_res > 0 && (!aligned64(k_res_fp16) || !aligned64(v_res_fp16))) return KVQ_ERR_ALIGN;
@@ -103,6 +108,23 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
     return launched(kvq::launch_decode(p, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                int32_t Hq, int32_t Hkv, const void *k_packed,
+                                const void *v_packed, int64_t packed_row_stride_bytes,
+                                int32_t n_packed_tokens, const void *k_res_fp16,
+                                const void *v_res_fp16, int32_t res_capacity, int32_t n_res,
+                                float sm_scale, int32_t num_splits, float *part_o,
+                                float *part_lse, hipStream_t stream)
+{
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, part_o, part_lse, stream);
 }
 
 kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,

@@ -276,3 +276,32 @@ def test_append_flush_loop_full(oracle_mod):
     assert np.array_equal(kp.cpu().numpy(), kp_ref)
     assert np.array_equal(vp.cpu().numpy(), vp_ref)
     assert np.array_equal(krd.cpu().numpy(), kr)
+
+
+@pytest.mark.parametrize("bits,hybrid", [(4, False), (2, True)])
+def test_decode_large_v_scales_take_exact_rescale(oracle_mod, bits, hybrid):
+    """V values of order 10^3 give V scales above 128, where the kernel must track the exact
+    running max (p * scale must stay inside fp16). Logits vary strongly (K x 3), so the
+    max moves between tiles. The output magnitude is ~10^3, so the bar is relative:
+    max error <= 2e-3 * max|out| and rel-L2 <= 1e-3."""
+    from gpu_common import dev, errors, gpu_decode, gpu_quantize
+    O = oracle_mod
+    rng = np.random.default_rng(21 + bits)
+    B, Hq, Hkv, n_packed, n_res, S_ = 1, 8, 2, 1024, 64, 3
+    q, ksrc, vsrc, kr, vr = _case(rng, B, Hq, Hkv, n_packed, n_res, "normal", 3.0)
+    vsrc = _f16(vsrc.astype(np.float32) * 400.0)
+    vr = _f16(vr.astype(np.float32) * 400.0)
+    fmt, ofmt = K.Format(bits, 128, hybrid), O.Format(bits, 128, hybrid)
+    rows = B * Hkv
+    kp_ref = O.quantize_pack(ofmt, ksrc.reshape(rows, n_packed, 128))
+    vp_ref = O.quantize_pack(ofmt, vsrc.reshape(rows, n_packed, 128))
+    scales = vp_ref.reshape(rows, -1, fmt.block_bytes)[:, :, fmt.sz_offset:fmt.sz_offset + 2048]
+    assert (scales.reshape(-1, 4).view(np.float16)[:, 0] >= 128).any()
+    print(f"[decode large V scales] bits={bits} hybrid={hybrid}", flush=True)
+    kp = gpu_quantize(fmt, ksrc.reshape(rows, n_packed, 128))
+    vp = gpu_quantize(fmt, vsrc.reshape(rows, n_packed, 128))
+    out, _, _ = gpu_decode(fmt, dev(q), Hkv, kp, vp, n_packed, dev(kr), dev(vr), n_res, S_, sm=SM)
+    ref = O.attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, sm=SM)
+    ma, rl = errors(out.cpu().numpy(), ref)
+    assert np.all(np.isfinite(out.cpu().numpy()))
+    assert ma <= 2e-3 * np.max(np.abs(ref)) and rl <= 1e-3, (ma, rl)
