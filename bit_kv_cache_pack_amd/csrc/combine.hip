@@ -14,35 +14,37 @@
 namespace kvq {
 namespace {
 
-// One workgroup of 256 threads per (batch, head). Thread t owns output channels
-// 4*(t % 32) .. +3 for the splits s = t / 32, t / 32 + 8, ...; it merges them in one pass
-// with its own running maximum (all of its loads can be in flight at once), and the eight
-// per-thread results of each channel are merged through LDS with the same rule.
+// Four workgroups of 128 threads per (batch, head), one per quarter of the channels, so
+// that 4 * B * Hq workgroups share the (latency-bound) work. Thread t owns the channels
+// 4 * (t % 8) .. +3 of its quarter for the splits s = t / 8, t / 8 + 16, ...: it first
+// takes the maximum of their lse, then sums w_s o_s and w_s with all loads independent;
+// the sixteen per-thread results of each channel are merged through LDS with the same
+// rule.
 template <bool F16>
-__global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ part_o,
+__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_lse, int S,
                                                       void *__restrict__ out)
 {
-    __shared__ float4_t red_o[8][32];
-    __shared__ float red_m[8], red_w[8];
+    constexpr int kGroups = 16;
+    __shared__ float4_t red_o[kGroups][8];
+    __shared__ float red_m[kGroups], red_w[kGroups];
     const int64_t bh = blockIdx.x;
+    const int quarter = blockIdx.y;
     const int t = threadIdx.x;
-    const int cq = t & 31, sg = t >> 5;
+    const int cq = t & 7, sg = t >> 3;
     const float *lse = part_lse + bh * S;
-    const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) + cq;
+    const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) +
+                        quarter * 8 + cq;
 
-    float m = -INFINITY, ws = 0.0f;
+    float m = -INFINITY;
+#pragma unroll 4
+    for (int s = sg; s < S; s += kGroups) m = fmaxf(m, lse[s]);
+    float ws = 0.0f;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int s = sg; s < S; s += 8) {
+#pragma unroll 4
+    for (int s = sg; s < S; s += kGroups) {
         const float ls = lse[s];
         const float4_t x = o[(int64_t)s * (kHeadDim / 4)];
-        if (ls > m) {                  // new running maximum: rescale what is accumulated
-            const float c = __expf(m - ls);
-            acc *= c;
-            ws *= c;
-            m = ls;
-        }
         const float w = ls == -INFINITY ? 0.0f : __expf(ls - m);
         acc += w * x;
         ws += w;
@@ -53,25 +55,26 @@ __global__ __launch_bounds__(256) void combine_kernel(const float *__restrict__ 
         red_w[sg] = ws;
     }
     __syncthreads();
-    if (t < 32) {
+    if (t < 8) {
         float M = red_m[0];
 #pragma unroll
-        for (int k = 1; k < 8; ++k) M = fmaxf(M, red_m[k]);
+        for (int k = 1; k < kGroups; ++k) M = fmaxf(M, red_m[k]);
         float4_t tot = {0.f, 0.f, 0.f, 0.f};
         float W = 0.0f;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
+        for (int k = 0; k < kGroups; ++k) {
             const float c = red_m[k] == -INFINITY ? 0.0f : __expf(red_m[k] - M);
             tot += c * red_o[k][t];
             W += c * red_w[k];
         }
         const float4_t r = tot / W;
+        const int64_t idx = bh * (kHeadDim / 4) + quarter * 8 + t;
         if (F16) {
             typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
             const half4_t h = {(_Float16)r[0], (_Float16)r[1], (_Float16)r[2], (_Float16)r[3]};
-            reinterpret_cast<half4_t *>(out)[bh * (kHeadDim / 4) + t] = h;
+            reinterpret_cast<half4_t *>(out)[idx] = h;
         } else {
-            reinterpret_cast<float4_t *>(out)[bh * (kHeadDim / 4) + t] = r;
+            reinterpret_cast<float4_t *>(out)[idx] = r;
         }
     }
 }
@@ -97,12 +100,12 @@ __global__ __launch_bounds__(32) void append_kernel(const uint16_t *__restrict__
 hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
                           int32_t num_splits, void *out, int32_t out_f16, hipStream_t stream)
 {
-    const dim3 grid((uint32_t)((int64_t)B * Hq));
+    const dim3 grid((uint32_t)((int64_t)B * Hq), 4);
     if (out_f16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(256), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(128), 0, stream, part_o, part_lse,
                            num_splits, out);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(256), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(128), 0, stream, part_o, part_lse,
                            num_splits, out);
     return hipGetLastError();
 }

@@ -13,13 +13,14 @@
 //    each wave streams 32-token tiles of the split (round robin) and keeps its own
 //    online-softmax state; the waves are merged through LDS at the end.
 //  * tiles reach LDS by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) into a
-//    2-slot ring per wave: a wave asks for its next two tiles up front and for tile k+2
-//    as soon as tile k is consumed, so ~10 KB per wave (120 KB per CU at three resident
-//    workgroups) is in flight without holding it in VGPRs; the wave waits on vmcnt for
+//    RING-slot ring per wave (RING = 2 or 3): a wave asks for its first two tiles up front
+//    and for tile k+2 once tile k is consumed (2 slots) or has arrived (3 slots), so ~10 KB
+//    per wave is in flight without holding it in VGPRs; the wave waits on vmcnt for
 //    exactly the tile it is about to use.
-//  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the raw integer codes (exact in fp16,
+//  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the integer codes plus 64 (exact in fp16,
 //    made with the fp16 magic-number trick) and rows i = 4*head + group of A holding the
-//    query restricted to one 32-channel group. Lane (token n, r) loads group r of token n
+//    query restricted to one 32-channel group; the accumulator starts at -64 * sum(q over
+//    the group), which removes the offset. Lane (token n, r) loads group r of token n
 //    (one 16/12/8-byte load), and MFMA o consumes that group's channel octet o, so the
 //    result row 4h+g is head h's dot product with group g's codes. Every lane then holds
 //    the four group dots of one (token, head) and applies its token's scale/zero:
@@ -27,11 +28,13 @@
 //    with no cross-lane reduction.
 //  * P V uses the same MFMA with rows i = 4*head + group holding p * scale_v (split into
 //    an fp16 high part and an fp16 remainder, two MFMAs, so the weights keep ~22 bits)
-//    and B = the V codes of 8 tokens x 1 channel per lane, built from two tokens' code
-//    words at a time. Only rows whose group matches the column's group are used; the
-//    zero-point term sum_t p_t zero_v is accumulated on the VALU.
-//  * row (16-lane) max / sum reductions use DPP; p and scale_v pass through a 1 KB
-//    per-wave LDS slice to reach the PV operand layout.
+//    and B = the V codes (plus 64) of 8 tokens x 1 channel per lane, built from two
+//    tokens' code words at a time. Only rows whose group matches the column's group are
+//    used; the zero-point term sum_t p_t zero'_v (zero' = zero - 64 * scale) is
+//    accumulated on the VALU.
+//  * row (16-lane) max / sum reductions use DPP; p passes through a 512 B per-wave LDS
+//    slice to reach the PV operand layout, and the V scales are read straight from the
+//    staged tile.
 #include "kvq_device.h"
 #include "kvq_internal.h"
 
@@ -40,6 +43,9 @@
 namespace kvq {
 namespace {
 
+#ifndef KVQ_DEEP_RING_MAX_WG
+#define KVQ_DEEP_RING_MAX_WG 512
+#endif
 constexpr int kWaves = 4;
 constexpr int kTile = 32;
 // a tile's max may exceed the running max by up to 2^kSlack before the accumulators are
@@ -64,20 +70,17 @@ struct DecArgs {
     int32_t block_bytes, sz_off;
 };
 
-constexpr int kRing = 2;
-
-// LDS of one workgroup, ~48 KB at 4 bits, so that three workgroups (12 waves) share a CU.
+// LDS of one workgroup: a RING-slot ring of tiles per wave plus small staging arrays
+// (4-bit: ~49 KB with 2 slots, three workgroups per CU; ~69 KB with 3 slots, two per CU).
 // A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
-template <int TILE_BYTES>
+template <int TILE_BYTES, int RING>
 struct Smem {
-    alignas(16) uint8_t ring[kWaves][kRing][TILE_BYTES];   // per-wave ring of staged tiles
+    alignas(16) uint8_t ring[kWaves][RING][TILE_BYTES];    // per-wave ring of staged tiles
     alignas(16) uint16_t q[kWaves][4][kHeadDim];            // per-wave copy of the chunk's q
-    alignas(16) float p[kWaves][4][kTile];    // p of head h, token t of the current tile
-    alignas(16) float sv[kWaves][4][kTile];   // V scale of group g, token t
+    alignas(16) float p[kWaves][2][4][kTile]; // p of head h, token t of tiles 2j and 2j+1
     alignas(16) float ml[kWaves][4][2];
     __device__ __forceinline__ float *mo(int w) { return reinterpret_cast<float *>(&ring[w][0][0]); }
 };
-static_assert(kRing * 1024 * 3 >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
 
 __device__ __forceinline__ void lds_fence()
 {
@@ -157,24 +160,28 @@ __device__ __forceinline__ void wait_vm()
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// wait until tile k is in LDS, when `after` (< kRing) younger tiles may still be in flight
+// wait until the oldest outstanding load group is in LDS, when `after` (0..3) younger
+// tiles may still be in flight behind it
 template <int BITS>
-__device__ __forceinline__ void wait_tile(int after)
+__device__ __forceinline__ void wait_behind(int after)
 {
     constexpr int NI = TileGeom<BITS>::NI;
-    static_assert(kRing == 2, "one younger tile at most");
-    if (after >= 1) wait_vm<NI>();
+    static_assert(3 * NI < 64, "vmcnt range");
+    if (after >= 3) wait_vm<3 * NI>();
+    else if (after == 2) wait_vm<2 * NI>();
+    else if (after == 1) wait_vm<NI>();
     else wait_vm<0>();
 }
 
-// wait for the q copy, requested before `tiles` (0..kRing) tiles
-template <int BITS>
-__device__ __forceinline__ void wait_q(int tiles)
+// Wave priority for instruction issue from the number of tiles the wave still has to
+// process (more left -> higher): without it the older of two workgroups sharing a CU wins
+// every issue conflict and the younger one finishes last.
+__device__ __forceinline__ void set_prio(int left)
 {
-    constexpr int NI = TileGeom<BITS>::NI;
-    if (tiles >= 2) wait_vm<2 * NI>();
-    else if (tiles == 1) wait_vm<NI>();
-    else wait_vm<0>();
+    if (left >= 4) __builtin_amdgcn_s_setprio(3);
+    else if (left == 3) __builtin_amdgcn_s_setprio(2);
+    else if (left == 2) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
 }
 
 // K codes of token t (0..31 in the tile), group r, as channel octets
@@ -255,11 +262,25 @@ __device__ __forceinline__ float sel4(float4_t v, int k)
     const float b = (k & 1) ? v[3] : v[2];
     return (k & 2) ? b : a;
 }
-__device__ __forceinline__ uint32_t sel4u(u32x4 v, int k)
+
+// fp16 pair {hi(p0 * s0), hi(p1 * s1)}: each product rounded once to fp16 (v_fma_mix with
+// the fp16 scale taken from the low half of a {scale, zero} dword)
+__device__ __forceinline__ uint32_t pv_hi(float p0, uint32_t s0, float p1, uint32_t s1)
 {
-    const uint32_t a = (k & 1) ? v[1] : v[0];
-    const uint32_t b = (k & 1) ? v[3] : v[2];
-    return (k & 2) ? b : a;
+    uint32_t d;
+    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(p0), "v"(s0));
+    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(d) : "v"(p1), "v"(s1));
+    return d;
+}
+// the fp16 of the remainders p0 * s0 - hi0 and p1 * s1 - hi1 (one rounding each)
+__device__ __forceinline__ uint32_t pv_lo(float p0, uint32_t s0, float p1, uint32_t s1, uint32_t hi)
+{
+    uint32_t d;
+    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]"
+        : "=v"(d) : "v"(p0), "v"(s0), "v"(hi));
+    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
+        : "+v"(d) : "v"(p1), "v"(s1), "v"(hi));
+    return d;
 }
 
 // Online-softmax state of one wave: lane (n, r) tracks head r.
@@ -269,76 +290,102 @@ struct WaveState {
     float4_t dpv[8];   // PV accumulators: rows 4h+g, column n <-> channel 8n + c
 };
 
-// Softmax update and PV for one 32-token tile. lg[u]: logits (exp2 domain) of token
-// 16u + n for head r; zv[u][g]: V zero-point term of that token; vpair[m][c]: the V
-// operand pair (slots 2m, 2m+1 of lane group r, i.e. tokens 8m + r and 8m + 4 + r;
-// channel 8n + c). The V scale of (token, group r) is already in sm.sv.
-template <int NH, class SM>
-__device__ __forceinline__ void softmax_pv(SM &sm, int wave, int n, int r, const float lg[2],
-                                           const float zv[2][4], const half2_t vpair[4][8],
-                                           bool big_scale, WaveState &st)
+// Stage A of a tile leaves these for stage B (per lane): the V code words of channel
+// octet n of tokens 4e + r, and the {scale_v, zero_v} dwords of tokens 4e + r, group gA
+// (the A-operand row of this lane).
+struct PVIn {
+    uint32_t vc[8];
+    uint32_t sd[8];
+};
+
+// Online-softmax step of stage A for one tile. lg[u]: logits (exp2 domain) of token 16u + n
+// for head r; zv[u][g]: V zero-point term of that token. Updates m, l and the zero-point
+// sums, returns the tile's p values, and leaves the factor the PV accumulators must be
+// multiplied by (once the previous tile's PV is in) in `alpha` when `rescale` is set.
+__device__ __forceinline__ void softmax_a(const float lg[2], const float zv[2][4], bool big_scale,
+                                          WaveState &st, float &p0, float &p1, float &alpha,
+                                          bool &rescale)
 {
     // Lazy rescale: the reference max m only moves when the tile's max exceeds it by more
     // than 2^kSlack (log2 units), or exceeds it at all while a V scale is so large that
     // p * scale could leave the fp16 range of the PV operand; otherwise p <= 2^kSlack.
     const float tmax = row_max16(fmaxf(lg[0], lg[1]));
     const bool grow = (tmax > st.m + kSlack) || (big_scale && tmax > st.m);
-    if (__builtin_amdgcn_ballot_w64(grow) != 0) {
-        const float mnew = grow ? tmax : st.m;
-        const float alpha = __builtin_amdgcn_exp2f(st.m - mnew);
-        st.m = mnew;
-        st.l *= alpha;
+    rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
+    const float mnew = grow ? tmax : st.m;
+    alpha = grow ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.0f;
+    st.m = mnew;
+    st.l *= alpha;
 #pragma unroll
-        for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
-    }
-    const float p0 = __builtin_amdgcn_exp2f(lg[0] - st.m);
-    const float p1 = __builtin_amdgcn_exp2f(lg[1] - st.m);
+    for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
+    p0 = __builtin_amdgcn_exp2f(lg[0] - st.m);
+    p1 = __builtin_amdgcn_exp2f(lg[1] - st.m);
     st.l += p0 + p1;
 #pragma unroll
     for (int g = 0; g < 4; ++g) st.zacc[g] = __builtin_fmaf(p1, zv[1][g], __builtin_fmaf(p0, zv[0][g], st.zacc[g]));
+}
 
-    sm.p[wave][r][slot_pos(n)] = p0;
-    sm.p[wave][r][slot_pos(16 + n)] = p1;
-    lds_fence();
-
-    // A operand of PV: lane (i, r) holds rows i = 4h + g, token slots 8r .. 8r+7
-    const int hA = n >> 2, gA = n & 3;
-    const float4_t pl = *reinterpret_cast<const float4_t *>(&sm.p[wave][hA][8 * r]);
-    const float4_t ph = *reinterpret_cast<const float4_t *>(&sm.p[wave][hA][8 * r + 4]);
-    const float4_t sl = *reinterpret_cast<const float4_t *>(&sm.sv[wave][gA][8 * r]);
-    const float4_t sh = *reinterpret_cast<const float4_t *>(&sm.sv[wave][gA][8 * r + 4]);
-    const float w[8] = {pl[0] * sl[0], pl[1] * sl[1], pl[2] * sl[2], pl[3] * sl[3],
-                        ph[0] * sh[0], ph[1] * sh[1], ph[2] * sh[2], ph[3] * sh[3]};
-    half8_t ahi, alo;
+// this lane's eight p values for stage B: head hA, token slots 8r .. 8r+7 (tokens 4e + r)
+__device__ __forceinline__ void load_p8(const float *pw, int n, int r, float p8[8])
+{
+    const int hA = n >> 2;
+    const float4_t pl = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r);
+    const float4_t ph = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r + 4);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float x = hA < NH ? w[e] : 0.0f;
-        const _Float16 hi = (_Float16)x;
-        ahi[e] = hi;
-        alo[e] = (_Float16)(x - (float)hi);
+    for (int e = 0; e < 4; ++e) {
+        p8[e] = pl[e];
+        p8[4 + e] = ph[e];
+    }
+}
+
+// Stage B core: PV for one tile. A operand: lane (i, r) holds rows i = 4h + g, token
+// slots 8r .. 8r+7, i.e. tokens 4e + r; the weight p * scale_v is split into an fp16 high
+// part and the fp16 of the remainder. vpair[m][c]: the V operand pair (slots 2m, 2m+1 of
+// lane group r, i.e. tokens 8m + r and 8m + 4 + r; channel 8n + c). (Rows of heads beyond
+// the chunk carry finite junk; their outputs are never stored.)
+__device__ __forceinline__ void pv_mfma(const float p8[8], const uint32_t sd[8],
+                                        const half2_t vpair[4][8], WaveState &st)
+{
+    u32x4 ahi, alo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        ahi[k] = pv_hi(p8[2 * k], sd[2 * k], p8[2 * k + 1], sd[2 * k + 1]);
+        alo[k] = pv_lo(p8[2 * k], sd[2 * k], p8[2 * k + 1], sd[2 * k + 1], ahi[k]);
     }
 #pragma unroll
     for (int c = 0; c < 8; ++c) {
         const half8_t bv{vpair[0][c].x, vpair[0][c].y, vpair[1][c].x, vpair[1][c].y,
                          vpair[2][c].x, vpair[2][c].y, vpair[3][c].x, vpair[3][c].y};
-        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ahi, bv, st.dpv[c], 0, 0, 0);
-        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(alo, bv, st.dpv[c], 0, 0, 0);
+        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi), bv,
+                                                           st.dpv[c], 0, 0, 0);
+        st.dpv[c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo), bv,
+                                                           st.dpv[c], 0, 0, 0);
     }
-    // the next tile rewrites sm.p / sm.sv only after these reads have returned
-    lds_fence();
 }
 
-template <int BITS, int NH, class SM>
-__device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const half8_t aq[4],
-                                            const float qs[4], float sm_log2, const Magic &M,
-                                            int wave, int n, int r, WaveState &st)
+template <int BITS>
+__device__ __forceinline__ void stage_b_packed(const float p8[8], const PVIn &pv, const Magic &M,
+                                               WaveState &st)
+{
+    half2_t vpair[4][8];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(pv.vc[2 * mm], pv.vc[2 * mm + 1], M, vpair[mm]);
+    pv_mfma(p8, pv.sd, vpair, st);
+}
+
+// Stage A of a packed tile in LDS slot `slot`: Q K^T, softmax step, p -> pw (this wave's
+// p buffer), and what stage B will need, copied out of the slot into registers.
+template <int BITS>
+__device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, const half8_t aq[4],
+                                               const float qs[4], const float4_t qinit,
+                                               float sm_log2, const Magic &M, int n, int r,
+                                               WaveState &st, PVIn &pv, float &alpha,
+                                               bool &rescale)
 {
     using G = TileGeom<BITS>;
+    const int gA = n & 3;
     KGroup<BITS> kc[2];
     u32x4 ksz[2], vsz[2];
-    uint32_t vc[8];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         kc[u].load(slot, 16 * u + n, r);
@@ -346,27 +393,36 @@ __device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const h
         vsz[u] = *reinterpret_cast<const u32x4 *>(slot + G::VSZ + (16 * u + n) * 16);
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) vc[e] = v_octet<BITS>(slot + G::CB, 4 * e + r, n);
+    for (int e = 0; e < 8; ++e) {
+        pv.vc[e] = v_octet<BITS>(slot + G::CB, 4 * e + r, n);
+        pv.sd[e] = *reinterpret_cast<const uint32_t *>(slot + G::VSZ + (4 * e + r) * 16 + 4 * gA);
+    }
 
     float lg[2], zv[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        float4_t acc = {0.f, 0.f, 0.f, 0.f};
+        // the K operand carries codes + 64; starting from -64 * sum(q over g) removes it
+        float4_t acc = qinit;
 #pragma unroll
         for (int o = 0; o < 4; ++o)
             acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[o], kc[u].octet(o, M), acc, 0, 0, 0);
-        float s = 0.0f;
+        // l = sum_g scale_g * dot_g + zero_g * sum(q over g), as two chains of two groups
+        float s01 = 0.0f, s23 = 0.0f;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+            const half2_t a = as_h2(ksz[u][g]), c = as_h2(ksz[u][g + 2]);
+            s01 = __builtin_fmaf((float)a.x, acc[g], s01);
+            s01 = __builtin_fmaf((float)a.y, qs[g], s01);
+            s23 = __builtin_fmaf((float)c.x, acc[g + 2], s23);
+            s23 = __builtin_fmaf((float)c.y, qs[g + 2], s23);
+        }
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-            const half2_t szk = as_h2(ksz[u][g]);
-            s = __builtin_fmaf((float)szk.x, acc[g], s);
-            s = __builtin_fmaf((float)szk.y, qs[g], s);
             const half2_t szv = as_h2(vsz[u][g]);
             // the V operand carries codes + 64: zero' = zero - 64 * scale
             zv[u][g] = __builtin_fmaf(-64.0f, (float)szv.x, (float)szv.y);
         }
-        lg[u] = s * sm_log2;
-        sm.sv[wave][r][slot_pos(16 * u + n)] = (float)as_h2(sel4u(vsz[u], r)).x;
+        lg[u] = (s01 + s23) * sm_log2;
     }
     // any V scale of the tile at or above 2^(15 - kSlack)? (fp16 compare on the low halves)
     bool big = false;
@@ -375,19 +431,27 @@ __device__ __forceinline__ void packed_tile(SM &sm, const uint8_t *slot, const h
 #pragma unroll
         for (int g = 0; g < 4; ++g) big |= as_h2(vsz[u][g]).x >= (_Float16)kBigScale;
     const bool big_scale = __builtin_amdgcn_ballot_w64(big) != 0;
-    half2_t vpair[4][8];
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(vc[2 * mm], vc[2 * mm + 1], M, vpair[mm]);
-    softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, big_scale, st);
+    float p0, p1;
+    softmax_a(lg, zv, big_scale, st, p0, p1, alpha, rescale);
+    pw[r * kTile + slot_pos(n)] = p0;
+    pw[r * kTile + slot_pos(16 + n)] = p1;
 }
 
-template <int BITS, int NH>
+__device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
+{
+#pragma unroll
+    for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
+}
+
+template <int BITS, int NH, int RING>
 __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
 {
     using G = TileGeom<BITS>;
-    __shared__ Smem<G::BYTES> sm;
+    static_assert(RING >= 2 && RING <= 3, "ring depth");
+    static_assert(RING * G::BYTES >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
+    __shared__ Smem<G::BYTES, RING> sm;
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int n = lane & 15;
     const int r = lane >> 4;
     const int64_t row = blockIdx.x;                 // b * Hkv + kvh
@@ -421,15 +485,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
     dma(rq, reinterpret_cast<uint8_t *>(&sm.q[wave][0][0]),
         (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
 
-    // ---- ask for this wave's first tiles ----
+    // ---- ask for this wave's first two tiles ----
     const int my_lo = tlo + wave;
     const int nt_w = my_lo < thi ? (thi - my_lo + kWaves - 1) / kWaves : 0;
     uint8_t *ring = &sm.ring[wave][0][0];
 #pragma unroll
-    for (int k = 0; k < kRing; ++k)
+    for (int k = 0; k < 2; ++k)
         if (k < nt_w) issue_tile<BITS>(rk, rv, ring + k * G::BYTES, my_lo + k * kWaves, lane,
                                        a.block_bytes, a.sz_off);
-    wait_q<BITS>(nt_w < kRing ? nt_w : kRing);
+    wait_behind<BITS>(nt_w < 2 ? nt_w : 2);           // q, issued before the tiles
 
     // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
     half8_t aq[4];
@@ -461,6 +525,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
         for (int g = 0; g < 4; ++g)
             qs[g] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * r + 4 * g) * 4, __float_as_int(s)));
     }
+    const float4_t qinit = {-64.0f * qs[0], -64.0f * qs[1], -64.0f * qs[2], -64.0f * qs[3]};
 
     const Magic M;
     WaveState st;
@@ -471,15 +536,63 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
 #pragma unroll
     for (int c = 0; c < 8; ++c) st.dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
 
-    // ---- packed tiles through the ring ----
-    for (int k = 0; k < nt_w; ++k) {
-        const int left = nt_w - 1 - k;                  // younger tiles possibly in flight
-        wait_tile<BITS>(left < kRing - 1 ? left : kRing - 1);
-        uint8_t *slot = ring + (k % kRing) * G::BYTES;
-        packed_tile<BITS, NH>(sm, slot, aq, qs, a.sm_log2, M, wave, n, r, st);
-        wait_lgkm0();                                    // the slot has been read
-        if (k + kRing < nt_w)
-            issue_tile<BITS>(rk, rv, slot, my_lo + (k + kRing) * kWaves, lane, a.block_bytes, a.sz_off);
+    // ---- packed tiles through the ring, software-pipelined ----
+    // Iteration k runs stage A (Q K^T, softmax, p) of tile k+1 next to stage B (P V) of
+    // tile k, so one wave has two independent chains of work. Two tiles are requested
+    // ahead: tile k+2 goes into the slot of tile k once stage A of tile k has read it
+    // (with three slots, as soon as tile k has arrived).
+    float *pbuf = &sm.p[wave][0][0][0];
+    const int pstride = 4 * kTile;
+    if (nt_w > 0) {
+        wait_behind<BITS>(nt_w > 1 ? 1 : 0);
+        if (RING == 3 && 2 < nt_w)
+            issue_tile<BITS>(rk, rv, ring + 2 * G::BYTES, my_lo + 2 * kWaves, lane, a.block_bytes, a.sz_off);
+        PVIn cur;
+        float alpha;
+        bool resc;
+        stage_a_packed<BITS>(ring, pbuf, aq, qs, qinit, a.sm_log2, M, n, r, st, cur, alpha, resc);
+        wait_lgkm0();                                    // slot 0 read, p of tile 0 written
+        if (RING == 2 && 2 < nt_w)
+            issue_tile<BITS>(rk, rv, ring, my_lo + 2 * kWaves, lane, a.block_bytes, a.sz_off);
+        // one pipeline step: stage A of tile k+1 (into `nxt`) next to stage B of tile k
+        auto step = [&](int k, const PVIn &cur, PVIn &nxt) {
+            wait_behind<BITS>(k + 2 < nt_w ? 1 : 0);    // tile k+1 in LDS; k+2 may be in flight
+            set_prio(nt_w - k);
+            const int s1 = (k + 1) % RING;
+            if (RING == 3 && k + 3 < nt_w)
+                issue_tile<BITS>(rk, rv, ring + ((k + 3) % RING) * G::BYTES,
+                                 my_lo + (k + 3) * kWaves, lane, a.block_bytes, a.sz_off);
+            float p8[8];
+            load_p8(pbuf + (k & 1) * pstride, n, r, p8);
+            stage_a_packed<BITS>(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, aq, qs,
+                                 qinit, a.sm_log2, M, n, r, st, nxt, alpha, resc);
+            stage_b_packed<BITS>(p8, cur, M, st);
+            if (resc) rescale_pv(st, alpha);             // tile k's PV is in; tile k+1 moved m
+            wait_lgkm0();                                // slot k+1 read, p of tile k+1 written
+            if (RING == 2 && k + 3 < nt_w)
+                issue_tile<BITS>(rk, rv, ring + s1 * G::BYTES, my_lo + (k + 3) * kWaves, lane,
+                                 a.block_bytes, a.sz_off);
+        };
+        auto last = [&](int k, const PVIn &cur) {
+            float p8[8];
+            load_p8(pbuf + (k & 1) * pstride, n, r, p8);
+            stage_b_packed<BITS>(p8, cur, M, st);
+            wait_lgkm0();
+        };
+        // two steps per trip so that the stage-A output and stage-B input swap roles
+        // instead of being copied
+        PVIn nxt;
+        int k = 0;
+        for (; k + 2 < nt_w; k += 2) {
+            step(k, cur, nxt);
+            step(k + 1, nxt, cur);
+        }
+        if (k + 1 < nt_w) {
+            step(k, cur, nxt);
+            last(k + 1, nxt);
+        } else {
+            last(k, cur);
+        }
     }
 
     // ---- residual / sink tokens (fp16), in 32-token tiles ----
@@ -503,7 +616,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 lg[u] = ts < a.n_res ? s * a.sm_log2 : -INFINITY;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zv[u][g] = 0.0f;
-                sm.sv[wave][r][slot_pos(16 * u + n)] = 1.0f;
             }
             u32x4 vt[8];
 #pragma unroll
@@ -519,7 +631,20 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
                 for (int c = 0; c < 8; ++c)
                     vpair[mm][c] = as_h2((c & 1) ? pack_hi16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1])
                                                  : pack_lo16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1]));
-            softmax_pv<NH>(sm, wave, n, r, lg, zv, vpair, false, st);
+            float p0, p1, alpha;
+            bool resc;
+            softmax_a(lg, zv, false, st, p0, p1, alpha, resc);
+            if (resc) rescale_pv(st, alpha);
+            pbuf[r * kTile + slot_pos(n)] = p0;
+            pbuf[r * kTile + slot_pos(16 + n)] = p1;
+            lds_fence();
+            float p8[8];
+            load_p8(pbuf, n, r, p8);
+            uint32_t ones[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) ones[e] = 0x3C00u;   // fp16 1.0: window tokens are not scaled
+            pv_mfma(p8, ones, vpair, st);
+            lds_fence();                                     // p read before the next tile rewrites it
         }
     }
 
@@ -579,11 +704,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
     }
 }
 
+// Three ring slots per wave (the next tiles are requested before the current one is
+// computed; two workgroups per CU at 4 bits) when the grid holds at most two workgroups per
+// CU of a 256-CU device; two slots (three workgroups per CU at 4 bits) for larger grids.
+inline bool deep_ring(int64_t workgroups) { return workgroups <= KVQ_DEEP_RING_MAX_WG; }
+
 template <int BITS, int NH>
 hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
 {
-    hipLaunchKernelGGL((decode_kernel<BITS, NH>),
-                       dim3((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks), dim3(256), 0, stream, a);
+    const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
+    if (deep_ring(rows * a.S * chunks))
+        hipLaunchKernelGGL((decode_kernel<BITS, NH, 3>), grid, dim3(256), 0, stream, a);
+    else
+        hipLaunchKernelGGL((decode_kernel<BITS, NH, 2>), grid, dim3(256), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -26,15 +26,21 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// max / sum over the 16 lanes of a row; every lane of the row gets the result
+// max over the 16 lanes of a row; every lane of the row gets the result. Each step is one
+// v_max_f32 with a DPP source (the s_nop covers the gfx9 hazard of a DPP read of a VGPR
+// written by the previous VALU instruction).
+#define KVQ_DPP_MAX(v, CTRL)                                                              \
+    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf"       \
+        : "=v"(v) : "v"(v))
 __device__ __forceinline__ float row_max16(float v)
 {
-    v = fmaxf(v, dpp_f<0x128>(v));
-    v = fmaxf(v, dpp_f<0x124>(v));
-    v = fmaxf(v, dpp_f<0x4E>(v));
-    v = fmaxf(v, dpp_f<0xB1>(v));
+    KVQ_DPP_MAX(v, "row_ror:8");
+    KVQ_DPP_MAX(v, "row_ror:4");
+    KVQ_DPP_MAX(v, "quad_perm:[2,3,0,1]");
+    KVQ_DPP_MAX(v, "quad_perm:[1,0,3,2]");
     return v;
 }
+// sum over the 16 lanes of a row; every lane of the row gets the result
 __device__ __forceinline__ float row_sum16(float v)
 {
     v = v + dpp_f<0x128>(v);
@@ -66,14 +72,11 @@ __device__ __forceinline__ uint32_t vconst(uint32_t c)
 }
 
 // fp16 magic-number conversion of small integer codes: OR-ing a code into the mantissa of
-// 2^E, at the bit whose weight is 1, gives the fp16 value 2^E + code exactly.
-//   base 0x6400 = 2^10 (code at bit 0), 0x5C00 = 2^8 (bit 2), 0x5800 = 2^7 (bit 3),
-//   0x5400 = 2^6 (bit 4), 0x4C00 = 2^4 (bit 6).
+// 2^6 (0x5400), at bits 4.. where one unit of the code weighs exactly 1, gives the fp16
+// value 64 + code exactly.
 struct Magic {
-    uint32_t b10, b8, b7, b6, b4;
-    __device__ __forceinline__ Magic()
-        : b10(vconst(0x64006400u)), b8(vconst(0x5C005C00u)), b7(vconst(0x58005800u)),
-          b6(vconst(0x54005400u)), b4(vconst(0x4C004C00u)) {}
+    uint32_t b6;
+    __device__ __forceinline__ Magic() : b6(vconst(0x54005400u)) {}
 };
 
 // two codes (one per 16-bit half) -> half2 of 2^E + code
@@ -81,23 +84,20 @@ __device__ __forceinline__ uint32_t mpair(uint32_t bits, uint32_t mask, uint32_t
 {
     return (bits & mask) | vbase;
 }
-// ... minus 2^E, exact: the codes themselves
-__device__ __forceinline__ half2_t mexact(uint32_t bits, uint32_t mask, uint32_t vbase, _Float16 e)
-{
-    return as_h2(mpair(bits, mask, vbase)) - half2_t{e, e};
-}
 
-// Eight codes of one 8-channel octet -> exact half8 in the slot order (0,4,1,5,2,6,3,7):
-// slot 2m holds channel m, slot 2m+1 holds channel m+4 (used for K, where the query
-// operand is laid out in the same order).
+// Eight codes of one 8-channel octet -> half8 of 64 + code, in the slot order
+// (0,4,1,5,2,6,3,7): slot 2m holds channel m, slot 2m+1 holds channel m+4 (used for K,
+// where the query operand is laid out in the same order). Every code is moved to the bits
+// whose weight at 2^6 is 1 (bits 4.. of each half), so all slots carry the same offset 64,
+// which the caller removes exactly through the accumulator (-64 * sum of q).
 //  4-bit: the octet is a 32-bit word, code i at bits 4i.
 __device__ __forceinline__ half8_t unpack_octet4(uint32_t w, const Magic &M)
 {
-    const uint32_t w8 = w >> 8;
-    const half2_t p0 = mexact(w, 0x000F000Fu, M.b10, (_Float16)1024.f);  // c0,c4
-    const half2_t p1 = mexact(w, 0x00F000F0u, M.b6, (_Float16)64.f);     // c1,c5
-    const half2_t p2 = mexact(w8, 0x000F000Fu, M.b10, (_Float16)1024.f); // c2,c6
-    const half2_t p3 = mexact(w8, 0x00F000F0u, M.b6, (_Float16)64.f);    // c3,c7
+    const uint32_t m = 0x00F000F0u;
+    const half2_t p0 = as_h2(mpair(w << 4, m, M.b6));   // c0,c4
+    const half2_t p1 = as_h2(mpair(w, m, M.b6));        // c1,c5
+    const half2_t p2 = as_h2(mpair(w >> 4, m, M.b6));   // c2,c6
+    const half2_t p3 = as_h2(mpair(w >> 8, m, M.b6));   // c3,c7
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 //  2-bit: the octet is 16 bits (low half of y), code i at bits 2i.
@@ -105,10 +105,11 @@ __device__ __forceinline__ half8_t unpack_octet2(uint32_t y, const Magic &M)
 {
     // c0..c3 (byte 0) stay in bits 0-7; c4..c7 (byte 1) move to bits 16-23
     const uint32_t w = perm_b32(0u, y, 0x0c010c00u);
-    const half2_t p0 = mexact(w, 0x00030003u, M.b10, (_Float16)1024.f);
-    const half2_t p1 = mexact(w, 0x000C000Cu, M.b8, (_Float16)256.f);
-    const half2_t p2 = mexact(w, 0x00300030u, M.b6, (_Float16)64.f);
-    const half2_t p3 = mexact(w, 0x00C000C0u, M.b4, (_Float16)16.f);
+    const uint32_t m = 0x00300030u;
+    const half2_t p0 = as_h2(mpair(w << 4, m, M.b6));
+    const half2_t p1 = as_h2(mpair(w << 2, m, M.b6));
+    const half2_t p2 = as_h2(mpair(w, m, M.b6));
+    const half2_t p3 = as_h2(mpair(w >> 2, m, M.b6));
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 //  3-bit: the octet is 24 bits (low bits of x), code i at bits 3i.
@@ -116,10 +117,11 @@ __device__ __forceinline__ half8_t unpack_octet3(uint32_t x, const Magic &M)
 {
     // c0..c3 (bits 0-11) stay; c4..c7 (bits 12-23) move to bits 16-27
     const uint32_t w = pack_lo16(x, x >> 12);
-    const half2_t p0 = mexact(w, 0x00070007u, M.b10, (_Float16)1024.f);
-    const half2_t p1 = mexact(w, 0x00380038u, M.b7, (_Float16)128.f);
-    const half2_t p2 = mexact(w, 0x01C001C0u, M.b4, (_Float16)16.f);
-    const half2_t p3 = mexact(w >> 3, 0x01C001C0u, M.b4, (_Float16)16.f);
+    const uint32_t m = 0x00700070u;
+    const half2_t p0 = as_h2(mpair(w << 4, m, M.b6));
+    const half2_t p1 = as_h2(mpair(w << 1, m, M.b6));
+    const half2_t p2 = as_h2(mpair(w >> 2, m, M.b6));
+    const half2_t p3 = as_h2(mpair(w >> 5, m, M.b6));
     return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
 }
 

@@ -35,6 +35,9 @@ class kvq_format(C.Structure):
                 ("hybrid", C.c_int32), ("block_tokens", C.c_int32)]
 
 
+_FMT_CACHE: dict = {}
+
+
 @dataclass(frozen=True)
 class Format:
     """Python view of kvq_format with the header's size helpers."""
@@ -45,8 +48,11 @@ class Format:
     block_tokens: int = 128
 
     def c(self) -> kvq_format:
-        return kvq_format(self.bits, self.head_dim, self.group, int(self.hybrid),
-                          self.block_tokens)
+        f = _FMT_CACHE.get(self)
+        if f is None:
+            f = _FMT_CACHE[self] = kvq_format(self.bits, self.head_dim, self.group,
+                                              int(self.hybrid), self.block_tokens)
+        return f
 
     @staticmethod
     def _a64(v: int) -> int:
