@@ -149,6 +149,11 @@ def main():
         K.kvq_decode_attention(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed, krd, vrd,
                                128, wl.n_res, sm, S_, part_o, part_lse, stream=sp)
 
+    def decode_valu(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_decode_attention_valu(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed,
+                                    krd, vrd, 128, wl.n_res, sm, S_, part_o, part_lse, stream=sp)
+
     def step(i, sp=sptr):
         decode(i, sp)
         K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
@@ -174,6 +179,8 @@ def main():
     # events (an upper bound on the kernel's own duration: it includes the gaps between
     # launches). This is the figure the roofline uses.
     dec_ms = timed(decode, args.steps, 5)
+    # the VALU-only comparison kernel (same partials, no matrix cores), timed the same way
+    valu_ms = timed(decode_valu, args.steps, 5)
     # the same K steps replayed from a HIP graph captured once, for reference
     cap_stream = torch.cuda.Stream(dev)
     g = torch.cuda.CUDAGraph()
@@ -247,6 +254,7 @@ def main():
         "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
         "us_per_step_graph_replay": round(graph_ms * 1e3, 3),
+        "decode_kernel_valu_only_us": round(valu_ms * 1e3, 3),
         "flush_us": round(flush_ms * 1e3, 3),
         "append_us": round(append_ms * 1e3, 3),
         "step_us_with_append_and_amortized_flush": round((ms_per_step + append_ms + flush_ms / 128)

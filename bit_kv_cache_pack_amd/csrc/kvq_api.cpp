@@ -62,7 +62,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
                          int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
                          const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
                          int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
-                         float *part_lse, hipStream_t stream)
+                         float *part_lse, hipStream_t stream, bool valu)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
@@ -107,7 +107,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.bits = fmt->bits;
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
-    return launched(kvq::launch_decode(p, stream));
+    return launched(valu ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
 }
 
 }  // namespace
@@ -124,7 +124,20 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream);
+                         num_splits, part_o, part_lse, stream, false);
+}
+
+kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                     int32_t Hq, int32_t Hkv, const void *k_packed,
+                                     const void *v_packed, int64_t packed_row_stride_bytes,
+                                     int32_t n_packed_tokens, const void *k_res_fp16,
+                                     const void *v_res_fp16, int32_t res_capacity,
+                                     int32_t n_res, float sm_scale, int32_t num_splits,
+                                     float *part_o, float *part_lse, hipStream_t stream)
+{
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, part_o, part_lse, stream, true);
 }
 
 kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,

@@ -21,7 +21,8 @@ _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
            -3: "unsupported format or shape", -4: "misaligned pointer or stride",
            -5: "kernel launch failed"}
 
-EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_combine", "kvq_append_residual")
+EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_valu",
+            "kvq_combine", "kvq_append_residual")
 
 
 class KVQError(RuntimeError):
@@ -99,6 +100,7 @@ def lib():
         L.kvq_quantize_pack.argtypes = [fp, vp, i64, i32, i64, i64, vp, i64, i32, vp]
         L.kvq_decode_attention.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32,
                                            i32, f32, i32, vp, vp, vp]
+        L.kvq_decode_attention_valu.argtypes = L.kvq_decode_attention.argtypes
         L.kvq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp]
         L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         for n in EXPORTED:
@@ -150,6 +152,19 @@ def kvq_decode_attention(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packe
                                     float(sm_scale), num_splits, _ptr(part_o), _ptr(part_lse),
                                     _stream(stream, q_fp16))
     _check("kvq_decode_attention", st)
+
+
+def kvq_decode_attention_valu(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
+                              v_packed, packed_row_stride_bytes: int, n_packed_tokens: int,
+                              k_res_fp16, v_res_fp16, res_capacity: int, n_res: int,
+                              sm_scale: float, num_splits: int, part_o, part_lse, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_valu(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_packed),
+                                         _ptr(v_packed), packed_row_stride_bytes,
+                                         n_packed_tokens, _ptr(k_res_fp16), _ptr(v_res_fp16),
+                                         res_capacity, n_res, float(sm_scale), num_splits,
+                                         _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
+    _check("kvq_decode_attention_valu", st)
 
 
 def kvq_combine(part_o, part_lse, B: int, Hq: int, head_dim: int, num_splits: int, out,

@@ -208,6 +208,21 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
                                 float *part_lse, hipStream_t stream);
 
 /*
+ * kvq_decode_attention_valu -- the same partials as kvq_decode_attention (same arguments,
+ * validation, errors and output layout; equal within floating-point rounding), computed
+ * with VALU dot products only (v_dot2_f32_f16, one query head per wave, no matrix cores).
+ * It is the measured comparison for the matrix-core design of kvq_decode_attention, whose
+ * use of MFMA for Q K^T and P V at GQA groups of 4 and more is justified by being faster.
+ */
+kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                     int32_t Hq, int32_t Hkv, const void *k_packed,
+                                     const void *v_packed, int64_t packed_row_stride_bytes,
+                                     int32_t n_packed_tokens, const void *k_res_fp16,
+                                     const void *v_res_fp16, int32_t res_capacity,
+                                     int32_t n_res, float sm_scale, int32_t num_splits,
+                                     float *part_o, float *part_lse, hipStream_t stream);
+
+/*
  * kvq_combine -- merge the split partials into the attention output (the log-sum-exp
  * merge of split-K flash-decoding, the FP16 baseline named in [BitDecoding] sec. 4.2):
  *   M = max_s lse_s, w_s = e^(lse_s - M), out = sum_s w_s o_s / sum_s w_s.

@@ -29,15 +29,18 @@ def gpu_quantize(fmt: K.Format, src16: np.ndarray, cap_blocks: int | None = None
 
 
 def gpu_decode(fmt: K.Format, q: torch.Tensor, Hkv: int, kp, vp, n_packed: int, kr, vr,
-               n_res: int, S: int, out_dtype: int = K.KVQ_OUT_F32, sm: float | None = None):
+               n_res: int, S: int, out_dtype: int = K.KVQ_OUT_F32, sm: float | None = None,
+               entry=None):
+    """Decode partials through `entry` (default kvq_decode_attention), then kvq_combine."""
+    entry = K.kvq_decode_attention if entry is None else entry
     B, Hq, d = q.shape
     sm = float(np.float32(1.0 / np.sqrt(d))) if sm is None else sm
     part_o = torch.empty((B, Hq, S, d), dtype=torch.float32, device=DEV)
     part_lse = torch.empty((B, Hq, S), dtype=torch.float32, device=DEV)
     stride = kp.shape[1] if kp is not None else 0
     cap = kr.shape[2] if kr is not None else 0
-    K.kvq_decode_attention(fmt, q, B, Hq, Hkv, kp, vp, stride, n_packed, kr, vr, cap, n_res, sm,
-                           S, part_o, part_lse)
+    entry(fmt, q, B, Hq, Hkv, kp, vp, stride, n_packed, kr, vr, cap, n_res, sm, S, part_o,
+          part_lse)
     out = torch.empty((B, Hq, d), dtype=torch.float16 if out_dtype == K.KVQ_OUT_F16
                       else torch.float32, device=DEV)
     K.kvq_combine(part_o, part_lse, B, Hq, d, S, out, out_dtype)

@@ -35,7 +35,7 @@ def _case(rng, B, Hq, Hkv, n_packed, n_res, dist="normal", scale=1.0, cap=128):
 
 
 def _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, dist="normal", scale=1.0,
-         seed=0, cap=128, check_partials=True):
+         seed=0, cap=128, check_partials=True, entry=None):
     from gpu_common import assert_close, dev, gpu_decode, gpu_quantize
     O = oracle_mod
     rng = np.random.default_rng(seed)
@@ -56,7 +56,8 @@ def _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, dist="normal
         kp_ref = vp_ref = np.zeros((rows, 0), np.uint8)
         kp = vp = None
     qd, krd, vrd = dev(q), dev(kr), dev(vr)
-    out, po, pl = gpu_decode(fmt, qd, Hkv, kp, vp, n_packed, krd, vrd, n_res, S_, sm=SM)
+    out, po, pl = gpu_decode(fmt, qd, Hkv, kp, vp, n_packed, krd, vrd, n_res, S_, sm=SM,
+                             entry=entry)
     torch.cuda.synchronize()
     ref = O.attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, sm=SM)
     res = assert_close(out.cpu().numpy(), ref, "attention")
@@ -182,7 +183,7 @@ def test_decode_rerun_is_deterministic():
 
 # ------------------------------------------------------------------ full workloads ----
 
-def _full(oracle_mod, name):
+def _full(oracle_mod, name, entry=None):
     from gpu_common import assert_close, bench_splits, dev, gpu_decode, gpu_quantize
     O = oracle_mod
     wl = S.WORKLOADS[name]
@@ -201,7 +202,7 @@ def _full(oracle_mod, name):
     S_ = bench_splits(wl)
     print(f"[decode full] {name}: decode S={S_}", flush=True)
     out, _, _ = gpu_decode(fmt, dev(x.q), wl.Hkv, kp, vp, wl.n_packed, dev(kr), dev(vr), wl.n_res,
-                           S_, sm=SM)
+                           S_, sm=SM, entry=entry)
     got = out.cpu().numpy()
     del kp, vp
     print(f"[decode full] {name}: oracle", flush=True)
