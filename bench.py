@@ -49,7 +49,7 @@ def parse():
 
 def kernel_source_digest() -> str:
     h = hashlib.sha256()
-    for f in ("decode_attn.hip", "kvq_device.h"):
+    for f in ("decode_attn.hip", "decode_common.h", "kvq_device.h"):
         with open(os.path.join(ROOT, "bit_kv_cache_pack_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -46,16 +46,18 @@ namespace {
 #ifndef KVQ_DEEP_RING_MAX_WG
 #define KVQ_DEEP_RING_MAX_WG 256
 #endif
-constexpr int kWaves = 4;
+#ifndef KVQ_WAVES
+#define KVQ_WAVES 4
+#endif
 // LDS of one workgroup: a RING-slot ring of tiles per wave plus small staging arrays
 // (4-bit: ~49 KB with 2 slots, three workgroups per CU; ~69 KB with 3 slots, two per CU).
 // A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
-template <int TILE_BYTES, int RING>
+template <int TILE_BYTES, int RING, int W>
 struct Smem {
-    alignas(16) uint8_t ring[kWaves][RING][TILE_BYTES];    // per-wave ring of staged tiles
-    alignas(16) uint16_t q[kWaves][4][kHeadDim];            // per-wave copy of the chunk's q
-    alignas(16) float p[kWaves][2][4][kTile]; // p of head h, token t of tiles 2j and 2j+1
-    alignas(16) float ml[kWaves][4][2];
+    alignas(16) uint8_t ring[W][RING][TILE_BYTES];    // per-wave ring of staged tiles
+    alignas(16) uint16_t q[W][4][kHeadDim];            // per-wave copy of the chunk's q
+    alignas(16) float p[W][2][4][kTile];      // p of head h, token t of tiles 2j and 2j+1
+    alignas(16) float ml[W][4][2];
     __device__ __forceinline__ float *mo(int w) { return reinterpret_cast<float *>(&ring[w][0][0]); }
 };
 
@@ -242,13 +244,14 @@ __device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
     for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
 }
 
-template <int BITS, int NH, int RING>
-__global__ __launch_bounds__(256) void decode_kernel(DecArgs a)
+template <int BITS, int NH, int RING, int W>
+__global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
 {
     using G = TileGeom<BITS>;
     static_assert(RING >= 2 && RING <= 3, "ring depth");
     static_assert(RING * G::BYTES >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
-    __shared__ Smem<G::BYTES, RING> sm;
+    constexpr int kWaves = W;
+    __shared__ Smem<G::BYTES, RING, W> sm;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int n = lane & 15;
@@ -505,10 +508,11 @@ template <int BITS, int NH>
 hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
 {
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
+    constexpr int W = KVQ_WAVES;
     if (deep_ring(rows * a.S * chunks))
-        hipLaunchKernelGGL((decode_kernel<BITS, NH, 3>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<BITS, NH, 3, W>), grid, dim3(64 * W), 0, stream, a);
     else
-        hipLaunchKernelGGL((decode_kernel<BITS, NH, 2>), grid, dim3(256), 0, stream, a);
+        hipLaunchKernelGGL((decode_kernel<BITS, NH, 2, W>), grid, dim3(64 * W), 0, stream, a);
     return hipGetLastError();
 }
 
