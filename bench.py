@@ -42,6 +42,7 @@ def parse():
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's suggestion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-fp16-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
     return ap.parse_args()
@@ -197,6 +198,38 @@ def main():
     graph_ms = t_start.elapsed_time(t_end) / args.steps
     del g
 
+    # FP16 flash-decoding baseline over the same tokens, uncompressed (the comparison the
+    # pages report their speed-ups against): kvq_decode_attention_fp16 + kvq_combine
+    fp16 = None
+    if not args.no_fp16_baseline:
+        f16_bytes = rows * wl.L * 128 * 2 * 2
+        copies_f = max(2, math.ceil(2 * MALL_BYTES / f16_bytes) + 1)
+        kf0 = torch.from_numpy(np.ascontiguousarray(x.k.reshape(rows, wl.L, 128))).to(dev)
+        vf0 = torch.from_numpy(np.ascontiguousarray(x.v.reshape(rows, wl.L, 128))).to(dev)
+        fcaches = [(kf0, vf0)] + [(kf0.clone(), vf0.clone()) for _ in range(copies_f - 1)]
+        S16 = K.suggest_splits(wl.B, wl.Hkv, wl.L, 128)     # one workgroup per CU (LDS)
+        po16 = torch.empty((wl.B, wl.Hq, S16, 128), dtype=torch.float32, device=dev)
+        pl16 = torch.empty((wl.B, wl.Hq, S16), dtype=torch.float32, device=dev)
+
+        def dec16(i, sp=sptr):
+            kf, vf = fcaches[i % copies_f]
+            K.kvq_decode_attention_fp16(q, wl.B, wl.Hq, wl.Hkv, kf, vf, wl.L, wl.L, sm, S16, po16,
+                                        pl16, stream=sp)
+
+        def step16(i, sp=sptr):
+            dec16(i, sp)
+            K.kvq_combine(po16, pl16, wl.B, wl.Hq, 128, S16, out, K.KVQ_OUT_F16, stream=sp)
+
+        f16_step_ms = timed(step16, args.steps, args.warmup)
+        f16_dec_ms = timed(dec16, args.steps, 5)
+        fp16 = {"splits": S16, "cache_copies": copies_f, "bytes_per_step": f16_bytes,
+                "us_per_step": round(f16_step_ms * 1e3, 3),
+                "decode_kernel_us": round(f16_dec_ms * 1e3, 3),
+                "GB_per_s_step": round(f16_bytes / (f16_step_ms * 1e-3) / 1e9, 2),
+                "speedup_of_packed_step": round(f16_step_ms / ms_per_step, 3),
+                "speedup_of_packed_decode_kernel": round(f16_dec_ms / dec_ms, 3)}
+        del fcaches, kf0, vf0
+
     # flush (quantize the full 128-token window of every row, K and V) and append
     fl_reps = 50
     fsrc = [(c[2], c[3]) for c in caches]
@@ -264,6 +297,7 @@ def main():
                    "bits": wl.bits, "group": 32, "hybrid": wl.hybrid, "n_packed": wl.n_packed,
                    "n_res": wl.n_res, "splits": S_, "cache_copies": copies,
                    "algorithmic_bytes_per_step": step_bytes},
+        "fp16_baseline": fp16,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (kvq_decode_attention)"},

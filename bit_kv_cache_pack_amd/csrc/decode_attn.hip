@@ -244,6 +244,67 @@ __device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
     for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
 }
 
+// Merge the W waves' states of one workgroup through LDS (sm.mo, sm.ml) and write the
+// split's partials: part_o (normalised) and part_lse (natural log) of the chunk's NH heads,
+// query head hq0 + h. Every wave of the workgroup must call it.
+template <int NH, int W, class SM>
+__device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wave, int n, int r,
+                                            float *part_o, float *part_lse, int64_t hq0, int S,
+                                            int split)
+{
+    const float lsum = row_sum16(st.l);
+    float zr[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) zr[g] = row_sum16(st.zacc[g]);
+    {
+        const int gj = n >> 2;   // group of channels 8n .. 8n+7
+        const float zg = sel4(float4_t{zr[0], zr[1], zr[2], zr[3]}, gj);
+        float4_t o0, o1;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            o0[c] = sel4(st.dpv[c], gj) + zg;
+            o1[c] = sel4(st.dpv[4 + c], gj) + zg;
+        }
+        float *mo = sm.mo(wave) + r * kHeadDim;
+        *reinterpret_cast<float4_t *>(mo + 8 * n) = o0;
+        *reinterpret_cast<float4_t *>(mo + 8 * n + 4) = o1;
+        if (n == 0) {
+            sm.ml[wave][r][0] = st.m;
+            sm.ml[wave][r][1] = lsum;
+        }
+    }
+    __syncthreads();
+    const int h = threadIdx.x >> 6;       // 4 heads x 64 threads x 2 channels
+    const int d = (threadIdx.x & 63) * 2;
+    if (h < NH) {
+        float Mx = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, sm.ml[w][h][0]);
+        float o0 = 0.f, o1 = 0.f, L = 0.f;
+        if (Mx != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < W; ++w) {
+                const float e = __builtin_amdgcn_exp2f(sm.ml[w][h][0] - Mx);
+                L += e * sm.ml[w][h][1];
+                o0 += e * sm.mo(w)[h * kHeadDim + d];
+                o1 += e * sm.mo(w)[h * kHeadDim + d + 1];
+            }
+        }
+        const int64_t hq = hq0 + h;
+        const int64_t ob = (hq * S + split) * kHeadDim + d;
+        float v0 = 0.f, v1 = 0.f, lse = -INFINITY;
+        if (L > 0.f) {
+            const float inv = 1.0f / L;
+            v0 = o0 * inv;
+            v1 = o1 * inv;
+            lse = (Mx + __log2f(L)) * 0.69314718055994531f;
+        }
+        part_o[ob] = v0;
+        part_o[ob + 1] = v1;
+        if (d == 0) part_lse[hq * S + split] = lse;
+    }
+}
+
 template <int BITS, int NH, int RING, int W>
 __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
 {
@@ -442,60 +503,153 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
         }
     }
 
-    // ---- merge the waves ----
-    const float lsum = row_sum16(st.l);
-    float zr[4];
+    // ---- merge the waves, write this split's partials ----
+    merge_store<NH, W>(sm, st, wave, n, r, a.part_o, a.part_lse, (int64_t)b * a.Hq + h0, a.S, split);
+}
+
+// ---------------------------------------------------------------------------------------
+// FP16 flash-decoding baseline: the same split-K partials from an uncompressed fp16 K/V
+// cache (rows of [tokens][128], token-major), the decode the packed cache is compared
+// against (BitDecoding page sec. 4.2 reports its speed-ups over FP16 decoding). Same
+// workgroup layout, ring of direct-to-LDS loads, MFMA Q K^T / P V and merge as the packed
+// kernel, with fp16 K and V operands in place of the codes.
+// ---------------------------------------------------------------------------------------
+constexpr int kF16TokB = kHeadDim * 2;                 // 256 B per token
+constexpr int kF16TileB = 2 * kTile * kF16TokB;        // K rows, then V rows: 16 KB
+constexpr int kF16NI = kF16TileB / 1024;               // 16 direct-to-LDS loads per tile
+
+__device__ __forceinline__ void issue_tile_f16(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                               uint8_t *slot, int tile, int lane)
+{
+    const uint32_t base = (uint32_t)tile * (kTile * kF16TokB);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) zr[g] = row_sum16(st.zacc[g]);
+    for (int k = 0; k < kTile * kF16TokB / 1024; ++k) {
+        dma(rk, slot + 1024 * k, base + 1024 * k + lane * 16, 16);
+        dma(rv, slot + kTile * kF16TokB + 1024 * k, base + 1024 * k + lane * 16, 16);
+    }
+}
+
+// wait until the oldest outstanding load group is in LDS with `after` (0..2) younger fp16
+// tiles still in flight behind it
+__device__ __forceinline__ void wait_behind_f16(int after)
+{
+    if (after >= 2) wait_vm<2 * kF16NI>();
+    else if (after == 1) wait_vm<kF16NI>();
+    else wait_vm<0>();
+}
+
+template <int NH, int W>
+__global__ __launch_bounds__(64 * W) void decode_f16_kernel(DecArgs a)
+{
+    constexpr int kWaves = W;
+    __shared__ Smem<kF16TileB, 2, W> sm;
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int n = lane & 15;
+    const int r = lane >> 4;
+    const int64_t row = blockIdx.x;
+    const int split = blockIdx.y;
+    const int b = (int)(row / a.Hkv);
+    const int kvh = (int)(row % a.Hkv);
+    const int h0 = kvh * a.gq + a.head_base + blockIdx.z * 4;
+
+    const int L = a.n_res;                             // tokens in the fp16 cache
+    const int NT = (L + kTile - 1) / kTile;
+    const int tlo = (int)((int64_t)split * NT / a.S);
+    const int thi = (int)((int64_t)(split + 1) * NT / a.S);
+
+    const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.kres + row * a.row_stride * kHeadDim), 0, a.row_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.vres + row * a.row_stride * kHeadDim), 0, a.row_bytes, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t *>(a.q), 0, a.q_bytes, kRsrcWord3);
+    dma(rq, reinterpret_cast<uint8_t *>(&sm.q[wave][0][0]),
+        (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
+
+    const int my_lo = tlo + wave;
+    const int nt_w = my_lo < thi ? (thi - my_lo + kWaves - 1) / kWaves : 0;
+    uint8_t *ring = &sm.ring[wave][0][0];
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+        if (k < nt_w) issue_tile_f16(rk, rv, ring + k * kF16TileB, my_lo + k * kWaves, lane);
+    wait_behind_f16(nt_w < 2 ? nt_w : 2);              // q, issued before the tiles
+
+    half8_t aq[4];
     {
-        const int gj = n >> 2;   // group of channels 8n .. 8n+7
-        const float zg = sel4(float4_t{zr[0], zr[1], zr[2], zr[3]}, gj);
-        float4_t o0, o1;
+        const int hA = n >> 2, gA = n & 3;
+        const bool live = (gA == r) && (hA < NH);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            o0[c] = sel4(st.dpv[c], gj) + zg;
-            o1[c] = sel4(st.dpv[4 + c], gj) + zg;
-        }
-        float *mo = sm.mo(wave) + r * kHeadDim;
-        *reinterpret_cast<float4_t *>(mo + 8 * n) = o0;
-        *reinterpret_cast<float4_t *>(mo + 8 * n + 4) = o1;
-        if (n == 0) {
-            sm.ml[wave][r][0] = st.m;
-            sm.ml[wave][r][1] = lsum;
+        for (int o = 0; o < 4; ++o) {
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hA][32 * r + 8 * o]);
+            aq[o] = live ? perm_octet_f16(w) : half8_t{};
         }
     }
-    __syncthreads();
-    {
-        const int h = threadIdx.x >> 6;       // 4 heads x 64 threads x 2 channels
-        const int d = (threadIdx.x & 63) * 2;
-        if (h < NH) {
-            float Mx = -INFINITY;
+    WaveState st;
+    st.m = -INFINITY;
+    st.l = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) Mx = fmaxf(Mx, sm.ml[w][h][0]);
-            float o0 = 0.f, o1 = 0.f, L = 0.f;
-            if (Mx != -INFINITY) {
+    for (int g = 0; g < 4; ++g) st.zacc[g] = 0.0f;
 #pragma unroll
-                for (int w = 0; w < kWaves; ++w) {
-                    const float e = __builtin_amdgcn_exp2f(sm.ml[w][h][0] - Mx);
-                    L += e * sm.ml[w][h][1];
-                    o0 += e * sm.mo(w)[h * kHeadDim + d];
-                    o1 += e * sm.mo(w)[h * kHeadDim + d + 1];
-                }
-            }
-            const int64_t hq = (int64_t)b * a.Hq + h0 + h;
-            const int64_t ob = (hq * a.S + split) * kHeadDim + d;
-            float v0 = 0.f, v1 = 0.f, lse = -INFINITY;
-            if (L > 0.f) {
-                const float inv = 1.0f / L;
-                v0 = o0 * inv;
-                v1 = o1 * inv;
-                lse = (Mx + __log2f(L)) * 0.69314718055994531f;
-            }
-            a.part_o[ob] = v0;
-            a.part_o[ob + 1] = v1;
-            if (d == 0) a.part_lse[hq * a.S + split] = lse;
+    for (int c = 0; c < 8; ++c) st.dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    float *pbuf = &sm.p[wave][0][0][0];
+    uint32_t ones[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) ones[e] = 0x3C00u;     // fp16 1.0: fp16 tokens are not scaled
+
+    for (int k = 0; k < nt_w; ++k) {
+        wait_behind_f16(k + 1 < nt_w ? 1 : 0);
+        set_prio(nt_w - k);
+        const uint8_t *slot = ring + (k & 1) * kF16TileB;
+        const int tok0 = (my_lo + k * kWaves) * kTile;
+        float lg[2], zv[2][4];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int t = 16 * u + n;
+            const uint8_t *kt = slot + t * kF16TokB + r * 64;
+            float4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int o = 0; o < 4; ++o)
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
+                    aq[o], perm_octet_f16(*reinterpret_cast<const u32x4 *>(kt + 16 * o)), acc, 0, 0, 0);
+            const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+            lg[u] = tok0 + t < L ? s * a.sm_log2 : -INFINITY;
+#pragma unroll
+            for (int g = 0; g < 4; ++g) zv[u][g] = 0.0f;
         }
+        u32x4 vt[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            vt[e] = *reinterpret_cast<const u32x4 *>(slot + kTile * kF16TokB + (4 * e + r) * kF16TokB + 16 * n);
+        half2_t vpair[4][8];
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                vpair[mm][c] = as_h2((c & 1) ? pack_hi16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1])
+                                             : pack_lo16(vt[2 * mm][c >> 1], vt[2 * mm + 1][c >> 1]));
+        float p0, p1, alpha;
+        bool resc;
+        softmax_a(lg, zv, false, st, p0, p1, alpha, resc);
+        if (resc) rescale_pv(st, alpha);
+        pbuf[r * kTile + slot_pos(n)] = p0;
+        pbuf[r * kTile + slot_pos(16 + n)] = p1;
+        lds_fence();
+        float p8[8];
+        load_p8(pbuf, n, r, p8);
+        pv_mfma(p8, ones, vpair, st);
+        wait_lgkm0();                                  // slot and p read
+        if (k + 2 < nt_w) issue_tile_f16(rk, rv, ring + (k & 1) * kF16TileB, my_lo + (k + 2) * kWaves, lane);
     }
+    merge_store<NH, W>(sm, st, wave, n, r, a.part_o, a.part_lse, (int64_t)b * a.Hq + h0, a.S, split);
+}
+
+template <int NH>
+hipError_t launch_f16_nh(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
+{
+    hipLaunchKernelGGL((decode_f16_kernel<NH, 4>), dim3((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks),
+                       dim3(256), 0, stream, a);
+    return hipGetLastError();
 }
 
 // Three ring slots per wave (the next tiles are requested before the current one is
@@ -538,7 +692,38 @@ hipError_t launch_nh(const DecArgs &a, int bits, int nh, int64_t rows, int chunk
     }
 }
 
+hipError_t launch_f16_heads(const DecArgs &a, int nh, int64_t rows, int chunks, hipStream_t stream)
+{
+    switch (nh) {
+    case 1: return launch_f16_nh<1>(a, rows, chunks, stream);
+    case 2: return launch_f16_nh<2>(a, rows, chunks, stream);
+    case 3: return launch_f16_nh<3>(a, rows, chunks, stream);
+    case 4: return launch_f16_nh<4>(a, rows, chunks, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 }  // namespace
+
+hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream)
+{
+    DecArgs a = make_dec_args(p);
+    a.row_stride = p.res_cap;                          // tokens between rows
+    a.row_bytes = (int32_t)((int64_t)p.n_res * kF16TokB);
+    const int64_t rows = (int64_t)p.B * p.Hkv;
+    const int full = a.gq / 4, tail = a.gq % 4;
+    hipError_t e = hipSuccess;
+    if (full > 0) {
+        a.head_base = 0;
+        e = launch_f16_heads(a, 4, rows, full, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) {
+        a.head_base = full * 4;
+        e = launch_f16_heads(a, tail, rows, 1, stream);
+    }
+    return e;
+}
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
 {

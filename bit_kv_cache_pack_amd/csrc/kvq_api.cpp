@@ -140,6 +140,42 @@ kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, 
                          num_splits, part_o, part_lse, stream, true);
 }
 
+kvq_status kvq_decode_attention_fp16(const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv,
+                                     const void *k_fp16, const void *v_fp16,
+                                     int64_t row_stride_tokens, int32_t n_tokens,
+                                     float sm_scale, int32_t num_splits, float *part_o,
+                                     float *part_lse, hipStream_t stream)
+{
+    if (!q_fp16 || !k_fp16 || !v_fp16 || !part_o || !part_lse) return KVQ_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return KVQ_ERR_SHAPE;
+    if (n_tokens < 1 || row_stride_tokens < n_tokens) return KVQ_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
+    if (!isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+    if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * 128 * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)n_tokens * 128 * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+    if (row_stride_tokens > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+    if (row_stride_tokens % 2 != 0) return KVQ_ERR_ALIGN;      // 512 B: keeps rows 64-B aligned
+    if (!aligned64(q_fp16) || !aligned64(k_fp16) || !aligned64(v_fp16) || !aligned64(part_o) ||
+        !aligned64(part_lse))
+        return KVQ_ERR_ALIGN;
+    kvq::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q_fp16);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.kres = static_cast<const uint16_t *>(k_fp16);
+    p.vres = static_cast<const uint16_t *>(v_fp16);
+    p.res_cap = (int32_t)row_stride_tokens;
+    p.n_res = n_tokens;
+    p.sm_scale = sm_scale;
+    p.num_splits = num_splits;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    return launched(kvq::launch_decode_f16(p, stream));
+}
+
 kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
                        int32_t head_dim, int32_t num_splits, void *out, int32_t out_dtype,
                        hipStream_t stream)

@@ -29,6 +29,7 @@ struct DecodeParams {
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
                           int32_t num_splits, void *out, int32_t out_f16, hipStream_t stream);

@@ -22,7 +22,7 @@ _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
            -5: "kernel launch failed"}
 
 EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_valu",
-            "kvq_combine", "kvq_append_residual")
+            "kvq_decode_attention_fp16", "kvq_combine", "kvq_append_residual")
 
 
 class KVQError(RuntimeError):
@@ -101,6 +101,8 @@ def lib():
         L.kvq_decode_attention.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32,
                                            i32, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_valu.argtypes = L.kvq_decode_attention.argtypes
+        L.kvq_decode_attention_fp16.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, f32, i32, vp,
+                                                vp, vp]
         L.kvq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp]
         L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         for n in EXPORTED:
@@ -165,6 +167,16 @@ def kvq_decode_attention_valu(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_
                                          res_capacity, n_res, float(sm_scale), num_splits,
                                          _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
     _check("kvq_decode_attention_valu", st)
+
+
+def kvq_decode_attention_fp16(q_fp16, B: int, Hq: int, Hkv: int, k_fp16, v_fp16,
+                              row_stride_tokens: int, n_tokens: int, sm_scale: float,
+                              num_splits: int, part_o, part_lse, stream=None):
+    st = lib().kvq_decode_attention_fp16(_ptr(q_fp16), B, Hq, Hkv, _ptr(k_fp16), _ptr(v_fp16),
+                                         row_stride_tokens, n_tokens, float(sm_scale),
+                                         num_splits, _ptr(part_o), _ptr(part_lse),
+                                         _stream(stream, q_fp16))
+    _check("kvq_decode_attention_fp16", st)
 
 
 def kvq_combine(part_o, part_lse, B: int, Hq: int, head_dim: int, num_splits: int, out,

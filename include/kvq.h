@@ -223,6 +223,25 @@ kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, 
                                      float *part_o, float *part_lse, hipStream_t stream);
 
 /*
+ * kvq_decode_attention_fp16 -- the split-K partials of one decode step over an
+ * uncompressed fp16 K/V cache: the FP16 flash-decoding baseline that the low-bit cache is
+ * compared against ([BitDecoding] sec. 4.1-4.2 report speed-ups over FP16 decoding).
+ *   q_fp16          [B][Hq][128]; head h reads kv-head h / (Hq/Hkv)
+ *   k_fp16, v_fp16  [B*Hkv][row_stride_tokens][128] fp16, token-major; tokens 0..n_tokens-1
+ *                   of every row are attended
+ *   row_stride_tokens  >= n_tokens, even (rows stay 64-byte aligned)
+ *   num_splits      S in 1..1024: with NT = ceil(n_tokens/32) tiles of 32 tokens, split s
+ *                   takes tiles [s*NT/S, (s+1)*NT/S); a split with no token has lse = -inf
+ *   part_o, part_lse  as for kvq_decode_attention; merge them with kvq_combine
+ * Supported: head_dim 128, 1 <= Hq/Hkv <= 16, n_tokens * 256 B < 2^31.
+ */
+kvq_status kvq_decode_attention_fp16(const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv,
+                                     const void *k_fp16, const void *v_fp16,
+                                     int64_t row_stride_tokens, int32_t n_tokens,
+                                     float sm_scale, int32_t num_splits, float *part_o,
+                                     float *part_lse, hipStream_t stream);
+
+/*
  * kvq_combine -- merge the split partials into the attention output (the log-sum-exp
  * merge of split-K flash-decoding, the FP16 baseline named in [BitDecoding] sec. 4.2):
  *   M = max_s lse_s, w_s = e^(lse_s - M), out = sum_s w_s o_s / sum_s w_s.

@@ -106,6 +106,31 @@ def test_decode_rejects(kw, status):
     assert _dec(**kw) == status
 
 
+def _f16(q=A, B=1, Hq=8, Hkv=2, k=A, v=A, stride=1024, n=1000, sm=0.088, S=4, po=A, pl=A):
+    return K.lib().kvq_decode_attention_fp16(q, B, Hq, Hkv, k, v, stride, n, sm, S, po, pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(k=None), K.KVQ_ERR_NULL),
+    (dict(pl=None), K.KVQ_ERR_NULL),
+    (dict(B=0), K.KVQ_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(n=0), K.KVQ_ERR_SHAPE),
+    (dict(stride=999), K.KVQ_ERR_SHAPE),            # stride below n_tokens
+    (dict(stride=1025), K.KVQ_ERR_ALIGN),           # odd stride
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(S=1025), K.KVQ_ERR_SHAPE),
+    (dict(sm=float("nan")), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(n=1 << 23, stride=1 << 23), K.KVQ_ERR_UNSUPPORTED),   # 2 GiB row
+    (dict(k=MIS), K.KVQ_ERR_ALIGN),
+    (dict(po=MIS), K.KVQ_ERR_ALIGN),
+])
+def test_fp16_decode_rejects(kw, status):
+    assert _f16(**kw) == status
+
+
 @pytest.mark.parametrize("args,status", [
     ((None, A, 1, 8, 128, 4, A, 0), K.KVQ_ERR_NULL),
     ((A, A, 1, 8, 128, 4, None, 0), K.KVQ_ERR_NULL),
