@@ -43,9 +43,6 @@
 namespace kvq {
 namespace {
 
-#ifndef KVQ_DEEP_RING_MAX_WG
-#define KVQ_DEEP_RING_MAX_WG 256
-#endif
 #ifndef KVQ_WAVES
 #define KVQ_WAVES 4
 #endif
@@ -309,7 +306,7 @@ template <int BITS, int NH, int RING, int W>
 __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
 {
     using G = TileGeom<BITS>;
-    static_assert(RING >= 2 && RING <= 3, "ring depth");
+    static_assert(RING >= 2 && RING <= 8, "ring depth");
     static_assert(RING * G::BYTES >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
     constexpr int kWaves = W;
     __shared__ Smem<G::BYTES, RING, W> sm;
@@ -340,15 +337,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
     dma(rq, reinterpret_cast<uint8_t *>(&sm.q[wave][0][0]),
         (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
 
-    // ---- ask for this wave's first two tiles ----
+    // ---- ask for this wave's first RING tiles ----
     const int my_lo = tlo + wave;
     const int nt_w = my_lo < thi ? (thi - my_lo + kWaves - 1) / kWaves : 0;
     uint8_t *ring = &sm.ring[wave][0][0];
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < RING; ++k)
         if (k < nt_w) issue_tile<BITS>(rk, rv, ring + k * G::BYTES, my_lo + k * kWaves, lane,
                                        a.block_bytes, a.sz_off);
-    wait_behind<BITS>(nt_w < 2 ? nt_w : 2);           // q, issued before the tiles
+    wait_behind<BITS>(nt_w < RING ? nt_w : RING);     // q, issued before the tiles
 
     // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
     half8_t aq[4];
@@ -393,30 +390,26 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
 
     // ---- packed tiles through the ring, software-pipelined ----
     // Iteration k runs stage A (Q K^T, softmax, p) of tile k+1 next to stage B (P V) of
-    // tile k, so one wave has two independent chains of work. Two tiles are requested
-    // ahead: tile k+2 goes into the slot of tile k once stage A of tile k has read it
-    // (with three slots, as soon as tile k has arrived).
+    // tile k, so one wave has two independent chains of work. RING tiles are requested up
+    // front; once stage A of tile j has read its slot, tile j + RING is requested into it,
+    // so RING - 1 tiles stay in flight behind the one being read.
     float *pbuf = &sm.p[wave][0][0][0];
     const int pstride = 4 * kTile;
     if (nt_w > 0) {
-        wait_behind<BITS>(nt_w > 1 ? 1 : 0);
-        if (RING == 3 && 2 < nt_w)
-            issue_tile<BITS>(rk, rv, ring + 2 * G::BYTES, my_lo + 2 * kWaves, lane, a.block_bytes, a.sz_off);
+        wait_behind<BITS>(nt_w - 1 < RING - 1 ? nt_w - 1 : RING - 1);
         PVIn cur;
         float alpha;
         bool resc;
         stage_a_packed<BITS>(ring, pbuf, aq, qs, qinit, a.sm_log2, M, n, r, st, cur, alpha, resc);
         wait_lgkm0();                                    // slot 0 read, p of tile 0 written
-        if (RING == 2 && 2 < nt_w)
-            issue_tile<BITS>(rk, rv, ring, my_lo + 2 * kWaves, lane, a.block_bytes, a.sz_off);
+        if (RING < nt_w)
+            issue_tile<BITS>(rk, rv, ring, my_lo + RING * kWaves, lane, a.block_bytes, a.sz_off);
         // one pipeline step: stage A of tile k+1 (into `nxt`) next to stage B of tile k
         auto step = [&](int k, const PVIn &cur, PVIn &nxt) {
-            wait_behind<BITS>(k + 2 < nt_w ? 1 : 0);    // tile k+1 in LDS; k+2 may be in flight
+            // tile k+1 in LDS; the tiles up to k+RING may still be in flight
+            wait_behind<BITS>(nt_w - 2 - k < RING - 1 ? nt_w - 2 - k : RING - 1);
             set_prio(nt_w - k);
             const int s1 = (k + 1) % RING;
-            if (RING == 3 && k + 3 < nt_w)
-                issue_tile<BITS>(rk, rv, ring + ((k + 3) % RING) * G::BYTES,
-                                 my_lo + (k + 3) * kWaves, lane, a.block_bytes, a.sz_off);
             float p8[8];
             load_p8(pbuf + (k & 1) * pstride, n, r, p8);
             stage_a_packed<BITS>(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, aq, qs,
@@ -424,9 +417,9 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
             stage_b_packed<BITS>(p8, cur, M, st);
             if (resc) rescale_pv(st, alpha);             // tile k's PV is in; tile k+1 moved m
             wait_lgkm0();                                // slot k+1 read, p of tile k+1 written
-            if (RING == 2 && k + 3 < nt_w)
-                issue_tile<BITS>(rk, rv, ring + s1 * G::BYTES, my_lo + (k + 3) * kWaves, lane,
-                                 a.block_bytes, a.sz_off);
+            if (k + 1 + RING < nt_w)
+                issue_tile<BITS>(rk, rv, ring + s1 * G::BYTES, my_lo + (k + 1 + RING) * kWaves,
+                                 lane, a.block_bytes, a.sz_off);
         };
         auto last = [&](int k, const PVIn &cur) {
             float p8[8];
@@ -652,22 +645,42 @@ hipError_t launch_f16_nh(const DecArgs &a, int64_t rows, int chunks, hipStream_t
     return hipGetLastError();
 }
 
-// Three ring slots per wave (the next tiles are requested before the current one is
-// computed; two workgroups per CU at 4 bits) when the grid holds at most one workgroup per
-// CU of a 256-CU device; otherwise two slots (three workgroups per CU at 4 bits), which
-// measured as fast or faster once two workgroups share a CU.
-inline bool deep_ring(int64_t workgroups) { return workgroups <= KVQ_DEEP_RING_MAX_WG; }
+#ifndef KVQ_RING
+#define KVQ_RING 2
+#endif
+// Ring depth per wave. Two slots (three workgroups per CU at 4 bits): deeper rings, which
+// keep more tiles in flight per wave but leave fewer waves per CU, measured slower at every
+// grid size tried (e.g. 16.6 us with 7 slots and one workgroup per CU against 12.4 us with
+// 2 slots at 32K tokens), because the first tiles arrive later and one wave per SIMD
+// computes its tiles more slowly.
+inline int ring_depth(int64_t workgroups, int bits)
+{
+    (void)workgroups;
+    (void)bits;
+    return KVQ_RING;
+}
+
+template <int BITS, int NH, int R>
+hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream)
+{
+    constexpr int W = KVQ_WAVES;
+    hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W>), grid, dim3(64 * W), 0, stream, a);
+    return hipGetLastError();
+}
 
 template <int BITS, int NH>
 hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
 {
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
-    constexpr int W = KVQ_WAVES;
-    if (deep_ring(rows * a.S * chunks))
-        hipLaunchKernelGGL((decode_kernel<BITS, NH, 3, W>), grid, dim3(64 * W), 0, stream, a);
-    else
-        hipLaunchKernelGGL((decode_kernel<BITS, NH, 2, W>), grid, dim3(64 * W), 0, stream, a);
-    return hipGetLastError();
+    switch (ring_depth(rows * a.S * chunks, BITS)) {
+    case 2: return launch_r<BITS, NH, 2>(a, grid, stream);
+    case 3: return launch_r<BITS, NH, 3>(a, grid, stream);
+    case 4: return launch_r<BITS, NH, 4>(a, grid, stream);
+    case 5: return launch_r<BITS, NH, 5>(a, grid, stream);
+    case 6: return launch_r<BITS, NH, 6>(a, grid, stream);
+    case 7: return launch_r<BITS, NH, 7>(a, grid, stream);
+    default: return launch_r<BITS, NH, (BITS == 4 ? 7 : 8)>(a, grid, stream);   // LDS bound
+    }
 }
 
 template <int BITS>

@@ -111,17 +111,23 @@ __device__ __forceinline__ void wait_vm()
 }
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 
-// wait until the oldest outstanding load group is in LDS, when `after` (0..3) younger
+// wait until the oldest outstanding load group is in LDS, when `after` (0..7) younger
 // tiles may still be in flight behind it
 template <int BITS>
 __device__ __forceinline__ void wait_behind(int after)
 {
     constexpr int NI = TileGeom<BITS>::NI;
-    static_assert(3 * NI < 64, "vmcnt range");
-    if (after >= 3) wait_vm<3 * NI>();
-    else if (after == 2) wait_vm<2 * NI>();
-    else if (after == 1) wait_vm<NI>();
-    else wait_vm<0>();
+    static_assert(7 * NI < 64, "vmcnt range");
+    switch (after < 7 ? after : 7) {
+    case 7: wait_vm<7 * NI>(); break;
+    case 6: wait_vm<6 * NI>(); break;
+    case 5: wait_vm<5 * NI>(); break;
+    case 4: wait_vm<4 * NI>(); break;
+    case 3: wait_vm<3 * NI>(); break;
+    case 2: wait_vm<2 * NI>(); break;
+    case 1: wait_vm<NI>(); break;
+    default: wait_vm<0>(); break;
+    }
 }
 
 // Wave priority for instruction issue from the number of tiles the wave still has to
