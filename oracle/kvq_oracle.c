@@ -21,7 +21,9 @@
  *      tokens kept at full precision (BitDecoding page, sec. 2.2; InnerQ page, sec. 2.3),
  *      in fp64, with the GQA head mapping of the BitDecoding page, sec. 2.3;
  *   5. the split-K form of the same attention (per-split max / sum / normalised output)
- *      and the log-sum-exp merge of the splits, in fp64.
+ *      and the log-sum-exp merge of the splits, in fp64;
+ *   6. key-channel normalization before quantization (InnerQ page, sec. 2.4): per-channel
+ *      norm = sqrt(max |K|) over the prefill keys, keys divided by it, queries multiplied.
  *
  * Floating point: every quantizer step is one IEEE binary32 operation with round to
  * nearest even (build with -O2 -ffp-contract=off, never -ffast-math). Attention is fp64.
@@ -593,4 +595,47 @@ void oq_split_range(int n_packed, int n_res, int S, int s, int64_t *lo, int64_t 
 {
     int wr;
     split_range(n_packed, n_res, S, s, lo, hi, &wr);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Key-channel normalization (InnerQ page, sec. 2.4): once, over the prefill keys, each  */
+/* channel i of a (batch, kv-head) gets norm_i = sqrt(max_t |K[t][i]|); keys are divided */
+/* by it and queries multiplied by it, which leaves every q . k, hence the softmax,      */
+/* unchanged while squeezing the spread between outlier and ordinary channels.           */
+/* Readings: the maximum runs over the tokens given (the prefill), per (row, channel);   */
+/* norm is the binary32 square root of that maximum, and 1 for an all-zero channel; the  */
+/* scaled value is the binary32 quotient (keys) or product (queries), rounded to fp16.   */
+/* ------------------------------------------------------------------------------------ */
+
+void oq_key_norm(const uint16_t *src, int64_t n_rows, int64_t n_tokens, int64_t row_stride,
+                 int64_t tok_stride, int head_dim, float *norm_out)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        for (int c = 0; c < head_dim; ++c) {
+            float mx = 0.0f;
+            for (int64_t t = 0; t < n_tokens; ++t) {
+                const float v = fabsf(oq_f16_to_f32(src[r * row_stride + t * tok_stride + c]));
+                if (v > mx) mx = v;
+            }
+            norm_out[r * head_dim + c] = mx > 0.0f ? sqrtf(mx) : 1.0f;
+        }
+    }
+}
+
+/* dst[r][t][c] = fp16(src[r][t][c] / norm[r / rows_per_norm][c])  (multiply == 0, keys)
+ *              = fp16(src[r][t][c] * norm[r / rows_per_norm][c])  (multiply != 0, queries) */
+void oq_channel_scale(const uint16_t *src, int64_t n_rows, int64_t n_tokens, int64_t row_stride,
+                      int64_t tok_stride, int head_dim, const float *norm, int64_t rows_per_norm,
+                      int multiply, uint16_t *dst, int64_t dst_row_stride, int64_t dst_tok_stride)
+{
+    for (int64_t r = 0; r < n_rows; ++r) {
+        const float *nr = norm + (r / rows_per_norm) * head_dim;
+        for (int64_t t = 0; t < n_tokens; ++t) {
+            for (int c = 0; c < head_dim; ++c) {
+                const float x = oq_f16_to_f32(src[r * row_stride + t * tok_stride + c]);
+                const float y = multiply ? x * nr[c] : x / nr[c];
+                dst[r * dst_row_stride + t * dst_tok_stride + c] = oq_f32_to_f16(y);
+            }
+        }
+    }
 }

@@ -72,6 +72,8 @@ def _setup(L):
                                      i32, i32, f64, i32, vp, vp, i32]
     L.oq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp]
     L.oq_split_range.argtypes = [i32, i32, i32, i32, C.POINTER(i64), C.POINTER(i64)]
+    L.oq_key_norm.argtypes = [vp, i64, i64, i64, i64, i32, vp]
+    L.oq_channel_scale.argtypes = [vp, i64, i64, i64, i64, i32, vp, i64, i32, vp, i64, i64]
 
 
 def default_threads() -> int:
@@ -293,3 +295,25 @@ def split_range(n_packed: int, n_res: int, S: int, s: int) -> tuple[int, int]:
     lo, hi = C.c_int64(), C.c_int64()
     lib().oq_split_range(n_packed, n_res, S, s, C.byref(lo), C.byref(hi))
     return lo.value, hi.value
+
+
+def key_norm(k16) -> np.ndarray:
+    """norm[rows][d] (float32) of key-channel normalization over k16[rows][T][d]."""
+    k = as_bits(k16)
+    rows, T, d = k.shape
+    k = np.ascontiguousarray(k)
+    out = np.zeros((rows, d), np.float32)
+    lib().oq_key_norm(_p(k), rows, T, T * d, d, d, _p(out))
+    return out
+
+
+def channel_scale(x16, norm, rows_per_norm: int = 1, multiply: bool = False) -> np.ndarray:
+    """fp16 bits of x / norm (keys) or x * norm (queries), x16[rows][T][d], per channel,
+    norm row r // rows_per_norm."""
+    x = np.ascontiguousarray(as_bits(x16))
+    rows, T, d = x.shape
+    nm = np.ascontiguousarray(norm, np.float32)
+    out = np.zeros_like(x)
+    lib().oq_channel_scale(_p(x), rows, T, T * d, d, d, _p(nm), rows_per_norm, int(multiply),
+                           _p(out), T * d, d)
+    return out
