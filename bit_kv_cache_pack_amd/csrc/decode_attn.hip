@@ -330,6 +330,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.vp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
 
+    // key-channel norms of this row's channels 8*(lane%16)..+7 when q is to be multiplied
+    // by them (loaded first, so they are older than every load waited for below)
+    float4_t qn0 = {}, qn1 = {};
+    if (a.qnorm) {
+        const float4_t *np = reinterpret_cast<const float4_t *>(a.qnorm + row * kHeadDim + 8 * n);
+        qn0 = np[0];
+        qn1 = np[1];
+    }
+
     // ---- q of the chunk's heads -> this wave's LDS copy (one 1 KB direct-to-LDS load,
     // issued before the tile requests so it is the oldest outstanding load) ----
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
@@ -346,6 +355,24 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
         if (k < nt_w) issue_tile<BITS>(rk, rv, ring + k * G::BYTES, my_lo + k * kWaves, lane,
                                        a.block_bytes, a.sz_off);
     wait_behind<BITS>(nt_w < RING ? nt_w : RING);     // q, issued before the tiles
+    if (a.qnorm) {
+        // q' = fp16(q * norm) per channel: lane (r, n) rescales the 16 bytes it loaded
+        // (head r of the chunk, channels 8n..8n+7) in place
+        u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.q[wave][r][8 * n]);
+        const u32x4 w = *mine;
+        const float nv[8] = {qn0[0], qn0[1], qn0[2], qn0[3], qn1[0], qn1[1], qn1[2], qn1[3]};
+        u32x4 o;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const half2_t h = as_h2(w[k]);
+            float y0 = (float)h.x * nv[2 * k], y1 = (float)h.y * nv[2 * k + 1];
+            asm("" : "+v"(y0), "+v"(y1));     // binary32 product, then its own fp16 rounding
+            o[k] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y0) |
+                   ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
+        }
+        *mine = o;
+        lds_fence();
+    }
 
     // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
     half8_t aq[4];

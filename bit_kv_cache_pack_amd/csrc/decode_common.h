@@ -31,6 +31,7 @@ struct DecArgs {
     int32_t S, Sp, res_alone;
     float *part_o, *part_lse;
     int32_t block_bytes, sz_off;
+    const float *qnorm;          // key-channel norms [rows][128] q is multiplied by, or null
 };
 
 __device__ __forceinline__ void lds_fence()
@@ -242,6 +243,7 @@ inline DecArgs make_dec_args(const DecodeParams &p)
     a.part_lse = p.part_lse;
     a.block_bytes = p.block_bytes;
     a.sz_off = p.sz_off;
+    a.qnorm = p.qnorm;
     a.row_bytes = (int32_t)((int64_t)(p.n_packed / kBlockTokens) * p.block_bytes);
     return a;
 }

@@ -62,7 +62,8 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
                          int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
                          const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
                          int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
-                         float *part_lse, hipStream_t stream, bool valu)
+                         float *part_lse, hipStream_t stream, bool valu,
+                         const float *qnorm = nullptr)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
@@ -107,6 +108,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.bits = fmt->bits;
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
+    p.qnorm = qnorm;
     return launched(valu ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
 }
 
@@ -125,6 +127,22 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
                          num_splits, part_o, part_lse, stream, false);
+}
+
+kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,
+                                      const float *key_norm, int32_t B, int32_t Hq,
+                                      int32_t Hkv, const void *k_packed, const void *v_packed,
+                                      int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
+                                      const void *k_res_fp16, const void *v_res_fp16,
+                                      int32_t res_capacity, int32_t n_res, float sm_scale,
+                                      int32_t num_splits, float *part_o, float *part_lse,
+                                      hipStream_t stream)
+{
+    if (!key_norm) return KVQ_ERR_NULL;
+    if (!aligned64(key_norm)) return KVQ_ERR_ALIGN;
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, part_o, part_lse, stream, false, key_norm);
 }
 
 kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -205,6 +223,46 @@ kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res
         static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
         static_cast<uint16_t *>(k_res), static_cast<uint16_t *>(v_res), B, Hkv, res_capacity,
         slot, stream));
+}
+
+kvq_status kvq_key_norm(const void *k_fp16, int64_t n_rows, int32_t n_tokens,
+                        int64_t row_stride, int64_t tok_stride, int32_t head_dim, float *norm,
+                        hipStream_t stream)
+{
+    if (!norm || (n_tokens > 0 && !k_fp16)) return KVQ_ERR_NULL;
+    if (n_rows < 1 || n_tokens < 0 || row_stride < 0 || tok_stride < head_dim)
+        return KVQ_ERR_SHAPE;
+    if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+    if ((n_rows * 128 + 255) / 256 > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (n_rows * ((n_tokens + 255) / 256) > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (row_stride % 8 != 0 || tok_stride % 8 != 0) return KVQ_ERR_ALIGN;
+    if (!aligned64(norm) || (n_tokens > 0 && !aligned64(k_fp16))) return KVQ_ERR_ALIGN;
+    return launched(kvq::launch_key_norm(static_cast<const uint16_t *>(k_fp16), n_rows, n_tokens,
+                                         row_stride, tok_stride, norm, stream));
+}
+
+kvq_status kvq_channel_scale(const void *x_fp16, int64_t n_rows, int32_t n_tokens,
+                             int64_t x_row_stride, int64_t x_tok_stride, int32_t head_dim,
+                             const float *norm, int64_t rows_per_norm, int32_t mode,
+                             void *y_fp16, int64_t y_row_stride, int64_t y_tok_stride,
+                             hipStream_t stream)
+{
+    if (!x_fp16 || !norm || !y_fp16) return KVQ_ERR_NULL;
+    if (n_rows < 1 || n_tokens < 0 || rows_per_norm < 1) return KVQ_ERR_SHAPE;
+    if (x_row_stride < 0 || y_row_stride < 0 || x_tok_stride < head_dim ||
+        y_tok_stride < head_dim)
+        return KVQ_ERR_SHAPE;
+    if (head_dim != 128) return KVQ_ERR_UNSUPPORTED;
+    if (mode != KVQ_SCALE_DIVIDE && mode != KVQ_SCALE_MULTIPLY) return KVQ_ERR_UNSUPPORTED;
+    if (n_rows * ((n_tokens + 63) / 64) > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (x_row_stride % 8 != 0 || x_tok_stride % 8 != 0 || y_row_stride % 8 != 0 ||
+        y_tok_stride % 8 != 0)
+        return KVQ_ERR_ALIGN;
+    if (!aligned64(x_fp16) || !aligned64(norm) || !aligned64(y_fp16)) return KVQ_ERR_ALIGN;
+    return launched(kvq::launch_channel_scale(
+        static_cast<const uint16_t *>(x_fp16), n_rows, n_tokens, x_row_stride, x_tok_stride, norm,
+        rows_per_norm, mode == KVQ_SCALE_MULTIPLY, static_cast<uint16_t *>(y_fp16), y_row_stride,
+        y_tok_stride, stream));
 }
 
 }  // extern "C"

@@ -25,6 +25,7 @@ struct DecodeParams {
     int32_t num_splits;
     float *part_o, *part_lse;
     int32_t bits, block_bytes, sz_off;
+    const float *qnorm;   // key-channel norms [B*Hkv][128] that q is multiplied by, or null
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
@@ -37,5 +38,14 @@ hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B,
 hipError_t launch_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
                          uint16_t *v_res, int32_t B, int32_t Hkv, int32_t res_cap, int32_t slot,
                          hipStream_t stream);
+
+hipError_t launch_key_norm(const uint16_t *k, int64_t n_rows, int32_t n_tokens,
+                           int64_t row_stride, int64_t tok_stride, float *norm,
+                           hipStream_t stream);
+
+hipError_t launch_channel_scale(const uint16_t *x, int64_t n_rows, int32_t n_tokens,
+                                int64_t x_row_stride, int64_t x_tok_stride, const float *norm,
+                                int64_t rows_per_norm, int multiply, uint16_t *y,
+                                int64_t y_row_stride, int64_t y_tok_stride, hipStream_t stream);
 
 }  // namespace kvq

@@ -17,12 +17,14 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5
 KVQ_OUT_F32, KVQ_OUT_F16 = 0, 1
+KVQ_SCALE_DIVIDE, KVQ_SCALE_MULTIPLY = 0, 1
 _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
            -3: "unsupported format or shape", -4: "misaligned pointer or stride",
            -5: "kernel launch failed"}
 
-EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_valu",
-            "kvq_decode_attention_fp16", "kvq_combine", "kvq_append_residual")
+EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_knorm",
+            "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
+            "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale")
 
 
 class KVQError(RuntimeError):
@@ -101,10 +103,15 @@ def lib():
         L.kvq_decode_attention.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32,
                                            i32, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_valu.argtypes = L.kvq_decode_attention.argtypes
+        L.kvq_decode_attention_knorm.argtypes = [fp, vp, vp, i32, i32, i32, vp, vp, i64, i32,
+                                                 vp, vp, i32, i32, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_fp16.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, f32, i32, vp,
                                                 vp, vp]
         L.kvq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp]
         L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.kvq_key_norm.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp]
+        L.kvq_channel_scale.argtypes = [vp, i64, i32, i64, i64, i32, vp, i64, i32, vp, i64, i64,
+                                        vp]
         for n in EXPORTED:
             getattr(L, n).restype = C.c_int
         _lib = L
@@ -156,6 +163,21 @@ def kvq_decode_attention(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packe
     _check("kvq_decode_attention", st)
 
 
+def kvq_decode_attention_knorm(fmt: Format, q_fp16, key_norm, B: int, Hq: int, Hkv: int,
+                               k_packed, v_packed, packed_row_stride_bytes: int,
+                               n_packed_tokens: int, k_res_fp16, v_res_fp16, res_capacity: int,
+                               n_res: int, sm_scale: float, num_splits: int, part_o, part_lse,
+                               stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_knorm(C.byref(f), _ptr(q_fp16), _ptr(key_norm), B, Hq, Hkv,
+                                          _ptr(k_packed), _ptr(v_packed),
+                                          packed_row_stride_bytes, n_packed_tokens,
+                                          _ptr(k_res_fp16), _ptr(v_res_fp16), res_capacity,
+                                          n_res, float(sm_scale), num_splits, _ptr(part_o),
+                                          _ptr(part_lse), _stream(stream, q_fp16))
+    _check("kvq_decode_attention_knorm", st)
+
+
 def kvq_decode_attention_valu(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
                               v_packed, packed_row_stride_bytes: int, n_packed_tokens: int,
                               k_res_fp16, v_res_fp16, res_capacity: int, n_res: int,
@@ -191,6 +213,22 @@ def kvq_append_residual(k_new, v_new, k_res, v_res, B: int, Hkv: int, head_dim: 
     st = lib().kvq_append_residual(_ptr(k_new), _ptr(v_new), _ptr(k_res), _ptr(v_res), B, Hkv,
                                    head_dim, res_capacity, slot, _stream(stream, k_new))
     _check("kvq_append_residual", st)
+
+
+def kvq_key_norm(k_fp16, n_rows: int, n_tokens: int, row_stride: int, tok_stride: int,
+                 head_dim: int, norm, stream=None):
+    st = lib().kvq_key_norm(_ptr(k_fp16), n_rows, n_tokens, row_stride, tok_stride, head_dim,
+                            _ptr(norm), _stream(stream, norm))
+    _check("kvq_key_norm", st)
+
+
+def kvq_channel_scale(x_fp16, n_rows: int, n_tokens: int, x_row_stride: int,
+                      x_tok_stride: int, head_dim: int, norm, rows_per_norm: int, mode: int,
+                      y_fp16, y_row_stride: int, y_tok_stride: int, stream=None):
+    st = lib().kvq_channel_scale(_ptr(x_fp16), n_rows, n_tokens, x_row_stride, x_tok_stride,
+                                 head_dim, _ptr(norm), rows_per_norm, mode, _ptr(y_fp16),
+                                 y_row_stride, y_tok_stride, _stream(stream, x_fp16))
+    _check("kvq_channel_scale", st)
 
 
 def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:

@@ -106,6 +106,8 @@ typedef struct {
 
 typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1 } kvq_out_dtype;
 
+typedef enum { KVQ_SCALE_DIVIDE = 0, KVQ_SCALE_MULTIPLY = 1 } kvq_scale_mode;
+
 /* ---- size helpers (header-only) ---- */
 static inline int64_t kvq_align64(int64_t v) { return (v + 63) / 64 * 64; }
 static inline int64_t kvq_codes_bytes(const kvq_format *f)
@@ -208,6 +210,27 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
                                 float *part_lse, hipStream_t stream);
 
 /*
+ * kvq_decode_attention_knorm -- kvq_decode_attention for a cache whose keys were
+ * key-channel normalized ([InnerQ] sec. 2.4, see kvq_key_norm): every query channel is first
+ * multiplied by the norm of its kv-head's row, q'[c] = fp16(q[c] * key_norm[b*Hkv + kvh][c])
+ * (binary32 product, round to nearest even), inside the decode kernel as it stages q. The
+ * partials are bit for bit those of kvq_channel_scale(q, KVQ_SCALE_MULTIPLY) followed by
+ * kvq_decode_attention on q', with no extra launch or q' buffer (the page folds the norm
+ * into the query projection for no run-time cost; this is the same for a caller that keeps
+ * its projection as is).
+ *   key_norm        fp32 [B*Hkv][128], 64-byte aligned (KVQ_ERR_NULL / KVQ_ERR_ALIGN)
+ *   other arguments, validation and outputs: as kvq_decode_attention.
+ */
+kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,
+                                      const float *key_norm, int32_t B, int32_t Hq,
+                                      int32_t Hkv, const void *k_packed, const void *v_packed,
+                                      int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
+                                      const void *k_res_fp16, const void *v_res_fp16,
+                                      int32_t res_capacity, int32_t n_res, float sm_scale,
+                                      int32_t num_splits, float *part_o, float *part_lse,
+                                      hipStream_t stream);
+
+/*
  * kvq_decode_attention_valu -- the same partials as kvq_decode_attention (same arguments,
  * validation, errors and output layout; equal within floating-point rounding), computed
  * with VALU dot products only (v_dot2_f32_f16, one query head per wave, no matrix cores).
@@ -264,6 +287,47 @@ kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, in
 kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res, void *v_res,
                                int32_t B, int32_t Hkv, int32_t head_dim, int32_t res_capacity,
                                int32_t slot, hipStream_t stream);
+
+/*
+ * kvq_key_norm -- key-channel normalization factors ([InnerQ] sec. 2.4): for every row r
+ * (one (batch, kv-head) of the K cache) and channel c,
+ *     norm[r][c] = sqrt(max_t |K_r[t][c]|)   over tokens t = 0..n_tokens-1 (the prefill keys),
+ * 1 where that maximum is 0. The maximum is exact (fp16 magnitudes); the square root is the
+ * correctly rounded binary32 one. Keys divided by these factors and queries multiplied by
+ * them (kvq_channel_scale, kvq_decode_attention_knorm) leave q . k unchanged up to fp16
+ * rounding while the range of outlier channels shrinks to its square root.
+ *   k_fp16          token t of row r at k + r*row_stride + t*tok_stride (elements), channels
+ *                   contiguous; strides multiples of 8 elements; may be NULL if n_tokens == 0
+ *   n_rows >= 1, n_tokens >= 0 (0: every factor is 1), head_dim must be 128
+ *   norm            fp32 [n_rows][128], written (also used as the reduction's workspace, so
+ *                   it must not alias k)
+ * Enqueues three small kernels; results are deterministic (a maximum does not depend on the
+ * order of its operands). Non-finite keys give undefined factors.
+ */
+kvq_status kvq_key_norm(const void *k_fp16, int64_t n_rows, int32_t n_tokens,
+                        int64_t row_stride, int64_t tok_stride, int32_t head_dim, float *norm,
+                        hipStream_t stream);
+
+/*
+ * kvq_channel_scale -- apply key-channel normalization factors ([InnerQ] sec. 2.4) to fp16
+ * vectors: for rows r, tokens t and channels c,
+ *     y[r][t][c] = fp16(x[r][t][c] / norm[r / rows_per_norm][c])   (KVQ_SCALE_DIVIDE: keys)
+ *     y[r][t][c] = fp16(x[r][t][c] * norm[r / rows_per_norm][c])   (KVQ_SCALE_MULTIPLY: queries)
+ * one binary32 operation (division correctly rounded) then round to nearest even.
+ *   x_fp16, y_fp16  token t of row r at base + r*row_stride + t*tok_stride (elements, per
+ *                   buffer); strides multiples of 8 elements. y may be x itself with the
+ *                   same strides (in place); any other overlap is undefined. Writing y into
+ *                   a residual window slot scales a new key on its way into the window.
+ *   n_rows >= 1, n_tokens >= 0 (0: nothing is enqueued), head_dim must be 128
+ *   norm            fp32 [n_rows / rows_per_norm rounded up][128] (kvq_key_norm's output)
+ *   rows_per_norm   >= 1: query rows [B][Hq] use rows_per_norm = Hq/Hkv so that head h of
+ *                   batch b takes the factors of kv-head h / (Hq/Hkv); key rows use 1
+ */
+kvq_status kvq_channel_scale(const void *x_fp16, int64_t n_rows, int32_t n_tokens,
+                             int64_t x_row_stride, int64_t x_tok_stride, int32_t head_dim,
+                             const float *norm, int64_t rows_per_norm, int32_t mode,
+                             void *y_fp16, int64_t y_row_stride, int64_t y_tok_stride,
+                             hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -174,3 +174,74 @@ def test_suggest_splits_bounds():
         s = K.suggest_splits(B, Hkv, n)
         assert 1 <= s <= 256
         assert s <= max(1, n // 32 // 8)
+
+
+def _dec_kn(fmt=None, q=A, norm=A, B=1, Hq=8, Hkv=2, kp=A, vp=A, stride=10240, n_packed=128,
+            kr=A, vr=A, cap=128, n_res=4, sm=0.088, S=4, po=A, pl=A):
+    f = _fmt() if fmt is None else fmt
+    return K.lib().kvq_decode_attention_knorm(C.byref(f), q, norm, B, Hq, Hkv, kp, vp, stride,
+                                              n_packed, kr, vr, cap, n_res, sm, S, po, pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(norm=None), K.KVQ_ERR_NULL),
+    (dict(norm=A + 16), K.KVQ_ERR_ALIGN),
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(fmt=_fmt(bits=7)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(n_packed=0, n_res=0), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(kp=MIS), K.KVQ_ERR_ALIGN),
+])
+def test_decode_knorm_rejects(kw, status):
+    assert _dec_kn(**kw) == status
+
+
+def _kn(k=A, rows=2, T=300, rs=512 * 128, ts=128, hd=128, norm=A):
+    return K.lib().kvq_key_norm(k, rows, T, rs, ts, hd, norm, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(norm=None), K.KVQ_ERR_NULL),
+    (dict(k=None), K.KVQ_ERR_NULL),
+    (dict(rows=0), K.KVQ_ERR_SHAPE),
+    (dict(T=-1), K.KVQ_ERR_SHAPE),
+    (dict(rs=-8), K.KVQ_ERR_SHAPE),
+    (dict(ts=64), K.KVQ_ERR_SHAPE),
+    (dict(hd=64, ts=64), K.KVQ_ERR_UNSUPPORTED),
+    (dict(ts=132), K.KVQ_ERR_ALIGN),
+    (dict(rs=512 * 128 + 4), K.KVQ_ERR_ALIGN),
+    (dict(k=MIS), K.KVQ_ERR_ALIGN),
+    (dict(norm=A + 32), K.KVQ_ERR_ALIGN),
+    (dict(rows=1 << 40), K.KVQ_ERR_SHAPE),
+])
+def test_key_norm_rejects(kw, status):
+    assert _kn(**kw) == status
+
+
+def _cs(x=A, rows=2, T=300, xrs=512 * 128, xts=128, hd=128, norm=A, rpn=1, mode=0, y=A,
+        yrs=512 * 128, yts=128):
+    return K.lib().kvq_channel_scale(x, rows, T, xrs, xts, hd, norm, rpn, mode, y, yrs, yts, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), K.KVQ_ERR_NULL),
+    (dict(norm=None), K.KVQ_ERR_NULL),
+    (dict(y=None), K.KVQ_ERR_NULL),
+    (dict(rows=0), K.KVQ_ERR_SHAPE),
+    (dict(T=-5), K.KVQ_ERR_SHAPE),
+    (dict(rpn=0), K.KVQ_ERR_SHAPE),
+    (dict(xts=120), K.KVQ_ERR_SHAPE),
+    (dict(yts=0), K.KVQ_ERR_SHAPE),
+    (dict(yrs=-8), K.KVQ_ERR_SHAPE),
+    (dict(hd=256, xts=256, yts=256), K.KVQ_ERR_UNSUPPORTED),
+    (dict(mode=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(xts=136 + 2), K.KVQ_ERR_ALIGN),
+    (dict(yrs=512 * 128 + 2), K.KVQ_ERR_ALIGN),
+    (dict(x=MIS), K.KVQ_ERR_ALIGN),
+    (dict(y=MIS), K.KVQ_ERR_ALIGN),
+    (dict(norm=A + 4), K.KVQ_ERR_ALIGN),
+    (dict(rows=1 << 40, T=1 << 20), K.KVQ_ERR_SHAPE),
+])
+def test_channel_scale_rejects(kw, status):
+    assert _cs(**kw) == status
