@@ -9,8 +9,9 @@ HIP graph are reported next to them.
 To keep the 256 MB Infinity Cache (MALL) from serving the reads, the timed loop rotates
 over enough independent copies of the packed cache to exceed 512 MB. Also measured, and
 reported next to the step: the flush (kvq_quantize_pack of the 128-token window of every
-row), the one-token append, a plain device copy as a bandwidth reference, and the CPU
-oracle on a bounded sample of the same workload.
+row), the one-token append, the key-channel normalization passes over the prefill keys and
+the decode step with normalized queries, the FP16 flash-decoding baseline, a plain device
+copy as a bandwidth reference, and the CPU oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
 """
@@ -43,6 +44,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-fp16-baseline", action="store_true")
+    ap.add_argument("--no-key-norm", action="store_true")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
     return ap.parse_args()
@@ -131,7 +133,7 @@ def main():
     vp0 = torch.empty_like(kp0)
     K.kvq_quantize_pack(fmt, kps_d, rows, wl.n_packed, wl.n_packed * 128, 128, kp0, nb * bb, 0)
     K.kvq_quantize_pack(fmt, vps_d, rows, wl.n_packed, wl.n_packed * 128, 128, vp0, nb * bb, 0)
-    del kps_d, vps_d
+    del vps_d
     step_bytes = wl.step_bytes()
     copies = args.copies or max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
     kr_d = torch.from_numpy(kr).to(dev)
@@ -230,6 +232,52 @@ def main():
                 "speedup_of_packed_decode_kernel": round(f16_dec_ms / dec_ms, 3)}
         del fcaches, kf0, vf0
 
+    # key-channel normalization: the once-per-prefill passes over the fp16 prefill keys
+    # (kvq_key_norm: 2 B read per element; kvq_channel_scale: 2 B read + 2 B written), and
+    # the decode step with q scaled inside the decode kernel (kvq_decode_attention_knorm)
+    knorm = None
+    if not args.no_key_norm:
+        kbytes = rows * wl.n_packed * 128 * 2
+        copies_k = max(2, math.ceil(2 * MALL_BYTES / kbytes) + 1)
+        ksrc = [kps_d] + [kps_d.clone() for _ in range(copies_k - 1)]
+        kdst = [torch.empty_like(kps_d) for _ in range(copies_k)]
+        nd = torch.empty((rows, 128), dtype=torch.float32, device=dev)
+        K.kvq_key_norm(kps_d, rows, wl.n_packed, wl.n_packed * 128, 128, 128, nd)
+
+        def key_norm(i, sp=sptr):
+            K.kvq_key_norm(ksrc[i % copies_k], rows, wl.n_packed, wl.n_packed * 128, 128, 128,
+                           nd, stream=sp)
+
+        def key_scale(i, sp=sptr):
+            K.kvq_channel_scale(ksrc[i % copies_k], rows, wl.n_packed, wl.n_packed * 128, 128,
+                                128, nd, 1, K.KVQ_SCALE_DIVIDE, kdst[i % copies_k],
+                                wl.n_packed * 128, 128, stream=sp)
+
+        def decode_kn(i, sp=sptr):
+            kp, vp, krd, vrd = caches[i % copies]
+            K.kvq_decode_attention_knorm(fmt, q, nd, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb,
+                                         wl.n_packed, krd, vrd, 128, wl.n_res, sm, S_, part_o,
+                                         part_lse, stream=sp)
+
+        def step_kn(i, sp=sptr):
+            decode_kn(i, sp)
+            K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+        reps = 50
+        kn_ms = timed(key_norm, reps, 3)
+        ks_ms = timed(key_scale, reps, 3)
+        step_kn_ms = timed(step_kn, args.steps, args.warmup)
+        dec_kn_ms = timed(decode_kn, args.steps, 5)
+        knorm = {"prefill_tokens": wl.n_packed, "key_bytes": kbytes, "copies": copies_k,
+                 "key_norm_us": round(kn_ms * 1e3, 3),
+                 "key_norm_GB_per_s": round(kbytes / (kn_ms * 1e-3) / 1e9, 1),
+                 "channel_scale_keys_us": round(ks_ms * 1e3, 3),
+                 "channel_scale_GB_per_s": round(2 * kbytes / (ks_ms * 1e-3) / 1e9, 1),
+                 "step_knorm_us": round(step_kn_ms * 1e3, 3),
+                 "decode_kernel_knorm_us": round(dec_kn_ms * 1e3, 3)}
+        del ksrc, kdst
+    del kps_d
+
     # flush (quantize the full 128-token window of every row, K and V) and append
     fl_reps = 50
     fsrc = [(c[2], c[3]) for c in caches]
@@ -298,6 +346,7 @@ def main():
                    "n_res": wl.n_res, "splits": S_, "cache_copies": copies,
                    "algorithmic_bytes_per_step": step_bytes},
         "fp16_baseline": fp16,
+        "key_norm": knorm,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (kvq_decode_attention)"},
