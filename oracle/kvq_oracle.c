@@ -639,3 +639,221 @@ void oq_channel_scale(const uint16_t *src, int64_t n_rows, int64_t n_tokens, int
         }
     }
 }
+
+/* ------------------------------------------------------------------------------------ */
+/* Paged cache with ragged lengths and a per-token sliding window.                       */
+/* InnerQ page sec. 2.3: a new token always enters the recent window; once the window is */
+/* full, its oldest token is quantized into the main (packed) cache; the sink window is  */
+/* filled at prefill and never changes. 3-bit blog page sec. 6.1: the packed cache is    */
+/* kept in pages of a uint8 pool reached through a per-sequence table.                   */
+/* Readings: packed token j of sequence b, kv-head h lives in pool block tbl[b][j / 128] */
+/* at pool + blk * block_stride + h * head_stride, token j % 128 of that block. Each     */
+/* sequence has a state {n_packed, n_res, next_slot, unused}: window slots             */
+/* [0, n_res) hold its fp16 tokens, slots [0, n_sink) are the sinks, and next_slot in    */
+/* [n_sink, res_cap) is the oldest recent token (the slots after the sinks are used as a */
+/* ring once the window is full). Lengths differ per sequence.                           */
+/* ------------------------------------------------------------------------------------ */
+
+static uint8_t *paged_block(uint8_t *pool, int64_t block_stride, int64_t head_stride,
+                            const int32_t *tbl, int max_blocks, int b, int h, int64_t j)
+{
+    const int64_t blk = tbl[(int64_t)b * max_blocks + j / OQ_BLOCK];
+    return pool + blk * block_stride + (int64_t)h * head_stride;
+}
+
+/* Quantize tokens t in [0, count[b]) of every (b, h) row of src into packed positions
+ * start[b] + t of sequence b (one token at a time, as the window eviction does). */
+void oq_pack_tokens_paged(int bits, int head_dim, int hybrid, const uint16_t *src, int B,
+                          int Hkv, int64_t src_row_stride, int64_t src_tok_stride,
+                          const int32_t *count, const int32_t *start, uint8_t *pool,
+                          int64_t block_stride, int64_t head_stride, const int32_t *tbl,
+                          int max_blocks)
+{
+    for (int b = 0; b < B; b++)
+        for (int h = 0; h < Hkv; h++)
+            for (int64_t t = 0; t < count[b]; t++) {
+                const int64_t j = (int64_t)start[b] + t;
+                quantize_token(src + ((int64_t)b * Hkv + h) * src_row_stride + t * src_tok_stride,
+                               bits, head_dim, hybrid,
+                               paged_block(pool, block_stride, head_stride, tbl, max_blocks, b,
+                                           h, j),
+                               (int)(j % OQ_BLOCK));
+            }
+}
+
+/* One decode-step update of every sequence's cache: if the window has a free slot the new
+ * token takes slot n_res; otherwise the oldest recent token (slot next_slot) is quantized
+ * into packed position n_packed, and the new token takes its slot. */
+void oq_append_evict(int bits, int head_dim, int hybrid, const uint16_t *k_new,
+                     const uint16_t *v_new, uint16_t *k_res, uint16_t *v_res, int res_cap,
+                     int n_sink, uint8_t *k_pool, uint8_t *v_pool, int64_t block_stride,
+                     int64_t head_stride, const int32_t *tbl, int max_blocks, int32_t *state,
+                     int B, int Hkv)
+{
+    const int d = head_dim;
+    for (int b = 0; b < B; b++) {
+        int32_t *st = state + 4 * (int64_t)b;
+        int slot;
+        if (st[1] < res_cap) {
+            slot = st[1];
+            st[1] += 1;
+        } else {
+            slot = st[2];
+            for (int h = 0; h < Hkv; h++) {
+                const int64_t w = (((int64_t)b * Hkv + h) * res_cap + slot) * d;
+                quantize_token(k_res + w, bits, d, hybrid,
+                               paged_block(k_pool, block_stride, head_stride, tbl, max_blocks,
+                                           b, h, st[0]),
+                               st[0] % OQ_BLOCK);
+                quantize_token(v_res + w, bits, d, hybrid,
+                               paged_block(v_pool, block_stride, head_stride, tbl, max_blocks,
+                                           b, h, st[0]),
+                               st[0] % OQ_BLOCK);
+            }
+            st[0] += 1;
+            st[2] = slot + 1 < res_cap ? slot + 1 : n_sink;
+        }
+        for (int h = 0; h < Hkv; h++) {
+            const int64_t w = (((int64_t)b * Hkv + h) * res_cap + slot) * d;
+            memcpy(k_res + w, k_new + ((int64_t)b * Hkv + h) * d, sizeof(uint16_t) * d);
+            memcpy(v_res + w, v_new + ((int64_t)b * Hkv + h) * d, sizeof(uint16_t) * d);
+        }
+    }
+}
+
+typedef struct {
+    int bits, head_dim, hybrid;
+    const uint16_t *q;
+    int B, Hq, Hkv;
+    const uint8_t *kpool, *vpool;
+    int64_t block_stride, head_stride;
+    const int32_t *tbl;
+    int max_blocks;
+    const int32_t *state;
+    const uint16_t *kres, *vres;
+    int res_cap;
+    double sm;
+    int S;
+    double *out, *lse;
+} patt_ctx;
+
+/* Token j of sequence b's order (packed 0..n_packed-1, then window slots 0..n_res-1). */
+static void paged_load_token(const patt_ctx *c, int b, int kvh, int64_t j, int which, double *x)
+{
+    const int64_t n_packed = c->state[4 * (int64_t)b];
+    if (j < n_packed) {
+        const uint8_t *blk = paged_block((uint8_t *)(which ? c->vpool : c->kpool),
+                                         c->block_stride, c->head_stride, c->tbl, c->max_blocks,
+                                         b, kvh, j);
+        dequant_token(blk, c->bits, c->head_dim, c->hybrid, j % OQ_BLOCK, x);
+    } else {
+        const int64_t slot = j - n_packed;
+        const uint16_t *r = (which ? c->vres : c->kres) +
+                            (((int64_t)b * c->Hkv + kvh) * c->res_cap + slot) * c->head_dim;
+        for (int i = 0; i < c->head_dim; i++)
+            x[i] = (double)oq_f16_to_f32(r[i]);
+    }
+}
+
+/* The fp64 softmax attention of head (b, h) over tokens [lo, hi) of its sequence. */
+static double paged_attend_range(const patt_ctx *c, int b, int h, int64_t lo, int64_t hi,
+                                 double *o)
+{
+    const int d = c->head_dim;
+    const int kvh = h / (c->Hq / c->Hkv);
+    for (int i = 0; i < d; i++) o[i] = 0.0;
+    if (hi <= lo) return -INFINITY;
+    const uint16_t *qh = c->q + ((int64_t)b * c->Hq + h) * d;
+    double *qd = malloc(sizeof(double) * d);
+    double *k = malloc(sizeof(double) * d), *v = malloc(sizeof(double) * d);
+    double *logit = malloc(sizeof(double) * (size_t)(hi - lo));
+    for (int i = 0; i < d; i++) qd[i] = (double)oq_f16_to_f32(qh[i]);
+    double m = -INFINITY;
+    for (int64_t j = lo; j < hi; j++) {
+        paged_load_token(c, b, kvh, j, 0, k);
+        double dot = 0.0;
+        for (int i = 0; i < d; i++) dot += qd[i] * k[i];
+        logit[j - lo] = c->sm * dot;
+        if (logit[j - lo] > m) m = logit[j - lo];
+    }
+    double l = 0.0;
+    for (int64_t j = lo; j < hi; j++) {
+        paged_load_token(c, b, kvh, j, 1, v);
+        const double p = exp(logit[j - lo] - m);
+        l += p;
+        for (int i = 0; i < d; i++) o[i] += p * v[i];
+    }
+    for (int i = 0; i < d; i++) o[i] /= l;
+    free(qd);
+    free(k);
+    free(v);
+    free(logit);
+    return m + log(l);
+}
+
+/*
+ * Split of a ragged sequence (restated from the interface contract): its packed tokens
+ * form NT = ceil(n_packed / 32) tiles, the last one possibly partial. With S > 1 and a
+ * non-empty window, split S-1 holds the window and splits 0..S-2 share the tiles;
+ * otherwise all S splits share the tiles and split S-1 also takes the window. Split s of
+ * the Sp sharing splits gets tiles [s*NT/Sp, (s+1)*NT/Sp), cut at n_packed.
+ */
+static void paged_split_range(int64_t n_packed, int64_t n_res, int S, int s, int64_t *lo,
+                              int64_t *hi)
+{
+    const int64_t NT = (n_packed + 31) / 32;
+    const int res_alone = (S > 1 && n_res > 0);
+    const int64_t Sp = res_alone ? S - 1 : S;
+    if (res_alone && s == S - 1) {
+        *lo = n_packed;
+        *hi = n_packed + n_res;
+        return;
+    }
+    *lo = 32 * (s * NT / Sp);
+    *hi = 32 * ((s + 1) * NT / Sp);
+    if (*lo > n_packed) *lo = n_packed;
+    if (*hi > n_packed) *hi = n_packed;
+    if (!res_alone && s == S - 1) *hi = n_packed + n_res;
+}
+
+static void patt_head(void *vctx, int64_t bh)
+{
+    const patt_ctx *c = (const patt_ctx *)vctx;
+    const int b = (int)(bh / c->Hq), h = (int)(bh % c->Hq);
+    const int64_t n = (int64_t)c->state[4 * (int64_t)b] + c->state[4 * (int64_t)b + 1];
+    paged_attend_range(c, b, h, 0, n, c->out + bh * c->head_dim);
+}
+
+static void patt_head_split(void *vctx, int64_t bh)
+{
+    const patt_ctx *c = (const patt_ctx *)vctx;
+    const int b = (int)(bh / c->Hq), h = (int)(bh % c->Hq);
+    for (int s = 0; s < c->S; s++) {
+        int64_t lo, hi;
+        paged_split_range(c->state[4 * (int64_t)b], c->state[4 * (int64_t)b + 1], c->S, s, &lo,
+                          &hi);
+        c->lse[bh * c->S + s] =
+            paged_attend_range(c, b, h, lo, hi, c->out + (bh * c->S + s) * c->head_dim);
+    }
+}
+
+/* out[B][Hq][d] over each sequence's own tokens (S == 0), or the split partials (S >= 1:
+ * part_o[B][Hq][S][d] into out, part_lse[B][Hq][S] into lse), fp64. */
+void oq_attention_paged(int bits, int head_dim, int hybrid, const uint16_t *q, int B, int Hq,
+                        int Hkv, const uint8_t *k_pool, const uint8_t *v_pool,
+                        int64_t block_stride, int64_t head_stride, const int32_t *tbl,
+                        int max_blocks, const int32_t *state, const uint16_t *kres,
+                        const uint16_t *vres, int res_cap, double sm, int S, double *out,
+                        double *lse, int n_threads)
+{
+    patt_ctx c = {bits, head_dim, hybrid, q, B, Hq, Hkv, k_pool, v_pool, block_stride,
+                  head_stride, tbl, max_blocks, state, kres, vres, res_cap, sm, S, out, lse};
+    oq_parallel_for((int64_t)B * Hq, n_threads, S ? patt_head_split : patt_head, &c);
+}
+
+/* Exposed for the tests: the token range [lo, hi) of split s of a ragged sequence. */
+void oq_paged_split_range(int64_t n_packed, int64_t n_res, int S, int s, int64_t *lo,
+                          int64_t *hi)
+{
+    paged_split_range(n_packed, n_res, S, s, lo, hi);
+}

@@ -74,6 +74,13 @@ def _setup(L):
     L.oq_split_range.argtypes = [i32, i32, i32, i32, C.POINTER(i64), C.POINTER(i64)]
     L.oq_key_norm.argtypes = [vp, i64, i64, i64, i64, i32, vp]
     L.oq_channel_scale.argtypes = [vp, i64, i64, i64, i64, i32, vp, i64, i32, vp, i64, i64]
+    L.oq_pack_tokens_paged.argtypes = [i32, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
+                                       i64, vp, i32]
+    L.oq_append_evict.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, vp,
+                                  i32, vp, i32, i32]
+    L.oq_attention_paged.argtypes = [i32, i32, i32, vp, i32, i32, i32, vp, vp, i64, i64, vp,
+                                     i32, vp, vp, vp, i32, f64, i32, vp, vp, i32]
+    L.oq_paged_split_range.argtypes = [i64, i64, i32, i32, C.POINTER(i64), C.POINTER(i64)]
 
 
 def default_threads() -> int:
@@ -317,3 +324,82 @@ def channel_scale(x16, norm, rows_per_norm: int = 1, multiply: bool = False) -> 
     lib().oq_channel_scale(_p(x), rows, T, T * d, d, d, _p(nm), rows_per_norm, int(multiply),
                            _p(out), T * d, d)
     return out
+
+
+# ---- paged cache, ragged lengths, per-token sliding window -------------------------------
+
+def _pool_strides(pool, block_stride, head_stride):
+    if block_stride is None or head_stride is None:
+        nblk, hkv, bb = pool.shape            # [n_blocks][Hkv][block_bytes]
+        return hkv * bb, bb
+    return block_stride, head_stride
+
+
+def _i32(a):
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def pack_tokens_paged(fmt: Format, src16, B: int, Hkv: int, count, start, pool, table,
+                      block_stride=None, head_stride=None):
+    """Quantize tokens [0, count[b]) of src16[B*Hkv][T][d] into packed positions
+    start[b] + t of each sequence's paged cache; `pool` (uint8) is written in place."""
+    src = np.ascontiguousarray(as_bits(src16))
+    rows, T, d = src.shape
+    assert rows == B * Hkv and pool.dtype == np.uint8 and pool.flags.c_contiguous
+    tbl = _i32(table)
+    bs, hs = _pool_strides(pool, block_stride, head_stride)
+    lib().oq_pack_tokens_paged(fmt.bits, d, int(fmt.hybrid), _p(src), B, Hkv, T * d, d,
+                               _p(_i32(count)), _p(_i32(start)), _p(pool), bs, hs, _p(tbl),
+                               tbl.shape[1])
+
+
+def append_evict(fmt: Format, k_new16, v_new16, k_res16, v_res16, n_sink: int, k_pool, v_pool,
+                 table, state, block_stride=None, head_stride=None):
+    """One decode-step window update with per-token eviction. k_res16/v_res16 (uint16 bits
+    or fp16, [B][Hkv][cap][d]), the pools and state ([B][4] int32) are updated in place."""
+    B, Hkv, cap, d = k_res16.shape
+    for a in (k_res16, v_res16, k_pool, v_pool, state):
+        assert a.flags.c_contiguous and a.flags.writeable
+    assert state.dtype == np.int32 and state.shape == (B, 4)
+    kn = np.ascontiguousarray(as_bits(k_new16))
+    vn = np.ascontiguousarray(as_bits(v_new16))
+    tbl = _i32(table)
+    bs, hs = _pool_strides(k_pool, block_stride, head_stride)
+    lib().oq_append_evict(fmt.bits, d, int(fmt.hybrid), _p(kn), _p(vn), _p(k_res16),
+                          _p(v_res16), cap, n_sink, _p(k_pool), _p(v_pool), bs, hs, _p(tbl),
+                          tbl.shape[1], _p(state), B, Hkv)
+
+
+def attention_paged(fmt: Format, q16, Hkv: int, k_pool, v_pool, table, state, k_res16, v_res16,
+                    sm: float | None = None, S: int = 0, block_stride=None, head_stride=None,
+                    n_threads: int | None = None):
+    """fp64 attention of every sequence over its own packed tokens (state[b][0] of them,
+    through the table) and window slots [0, state[b][1]). S == 0: out[B][Hq][d];
+    S >= 1: the split partials (part_o[B][Hq][S][d], part_lse[B][Hq][S])."""
+    q = np.ascontiguousarray(as_bits(q16))
+    B, Hq, d = q.shape
+    kr = np.ascontiguousarray(as_bits(k_res16))
+    vr = np.ascontiguousarray(as_bits(v_res16))
+    cap = kr.shape[2]
+    tbl = _i32(table)
+    st = _i32(state)
+    bs, hs = _pool_strides(k_pool, block_stride, head_stride)
+    sm = float(np.float32(1.0 / np.sqrt(d))) if sm is None else sm
+    kp = np.ascontiguousarray(k_pool)
+    vp = np.ascontiguousarray(v_pool)
+    if S == 0:
+        out = np.zeros((B, Hq, d), np.float64)
+        lse = np.zeros(1, np.float64)
+    else:
+        out = np.zeros((B, Hq, S, d), np.float64)
+        lse = np.zeros((B, Hq, S), np.float64)
+    lib().oq_attention_paged(fmt.bits, d, int(fmt.hybrid), _p(q), B, Hq, Hkv, _p(kp), _p(vp),
+                             bs, hs, _p(tbl), tbl.shape[1], _p(st), _p(kr), _p(vr), cap, sm, S,
+                             _p(out), _p(lse), n_threads or default_threads())
+    return out if S == 0 else (out, lse)
+
+
+def paged_split_range(n_packed: int, n_res: int, S: int, s: int) -> tuple[int, int]:
+    lo, hi = C.c_int64(), C.c_int64()
+    lib().oq_paged_split_range(n_packed, n_res, S, s, C.byref(lo), C.byref(hi))
+    return lo.value, hi.value
