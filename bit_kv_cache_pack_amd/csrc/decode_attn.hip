@@ -172,13 +172,14 @@ __device__ __forceinline__ void stage_b_packed(const float p8[8], const PVIn &pv
 }
 
 // Stage A of a packed tile in LDS slot `slot`: Q K^T, softmax step, p -> pw (this wave's
-// p buffer), and what stage B will need, copied out of the slot into registers.
-template <int BITS>
+// p buffer), and what stage B will need, copied out of the slot into registers. With MASK,
+// tokens nvalid .. 31 of the tile are not attended (their logits are -inf).
+template <int BITS, bool MASK = false>
 __device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, const half8_t aq[4],
                                                const float qs[4], const float4_t qinit,
                                                float sm_log2, const Magic &M, int n, int r,
                                                WaveState &st, PVIn &pv, float &alpha,
-                                               bool &rescale)
+                                               bool &rescale, int nvalid = kTile)
 {
     using G = TileGeom<BITS>;
     const int gA = n & 3;
@@ -221,6 +222,7 @@ __device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, c
             zv[u][g] = __builtin_fmaf(-64.0f, (float)szv.x, (float)szv.y);
         }
         lg[u] = (s01 + s23) * sm_log2;
+        if (MASK && 16 * u + n >= nvalid) lg[u] = -INFINITY;
     }
     // any V scale of the tile at or above 2^(15 - kSlack)? (fp16 compare on the low halves)
     bool big = false;
@@ -302,8 +304,10 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
     }
 }
 
-template <int BITS, int NH, int RING, int W>
-__global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
+template <int BITS, int NH, int RING, int W, bool PAGED>
+__global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
+                                                        const int32_t *__restrict__ tbl,
+                                                        const int32_t *__restrict__ seq_state)
 {
     using G = TileGeom<BITS>;
     static_assert(RING >= 2 && RING <= 8, "ring depth");
@@ -320,15 +324,62 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
     const int kvh = (int)(row % a.Hkv);
     const int h0 = kvh * a.gq + a.head_base + blockIdx.z * 4;   // first query head of the chunk
 
+    // ---- this sequence's lengths (a paged cache has its own per sequence) ----
+    int n_packed_b = a.n_packed, n_res_b = a.n_res;
+    if constexpr (PAGED) {
+        n_packed_b = __builtin_amdgcn_readfirstlane(seq_state[4 * (int64_t)b]);
+        n_res_b = __builtin_amdgcn_readfirstlane(seq_state[4 * (int64_t)b + 1]);
+        // out-of-range lengths are clamped (never an access outside the table or window)
+        const int cap_p = a.max_blocks * kBlockTokens;
+        n_packed_b = n_packed_b < 0 ? 0 : (n_packed_b > cap_p ? cap_p : n_packed_b);
+        n_res_b = n_res_b < 0 ? 0 : (n_res_b > a.res_cap ? a.res_cap : n_res_b);
+    }
+
     // ---- token range of this split (same rule as the header documents) ----
     int tlo, thi;
     bool with_res;
-    split_range(a, split, tlo, thi, with_res);
+    if constexpr (PAGED)
+        split_range_seq(a, split, n_packed_b, n_res_b, tlo, thi, with_res);
+    else
+        split_range(a, split, tlo, thi, with_res);
 
     const __amdgpu_buffer_rsrc_t rk = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.kp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.vp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
+    // request tile `tile` of this row into `slot`: from the contiguous row, or from the
+    // pool block the table names (a block id outside the pool reads block 0 instead)
+    auto issue = [&](uint8_t *slot, int tile) {
+        if constexpr (PAGED) {
+            int64_t blk = __builtin_amdgcn_readfirstlane(tbl[(int64_t)b * a.max_blocks + (tile >> 2)]);
+            if (blk < 0 || blk >= a.pool_blocks) blk = 0;
+            const int64_t off = blk * a.block_stride + (int64_t)kvh * a.head_stride;
+            const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(a.kp + off), 0, a.block_bytes, kRsrcWord3);
+            const __amdgpu_buffer_rsrc_t rvt = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint8_t *>(a.vp + off), 0, a.block_bytes, kRsrcWord3);
+            issue_tile_at<BITS>(rkt, rvt, slot, 0u, (tile & 3) * kTile, lane, a.sz_off);
+        } else {
+            issue_tile<BITS>(rk, rv, slot, tile, lane, a.block_bytes, a.sz_off);
+        }
+    };
+    // the last tile of a ragged sequence: its missing tokens get scale/zero 0 in LDS (the
+    // bytes behind them may be anything) and are masked out of the softmax
+    const int nt_seq = (n_packed_b + kTile - 1) / kTile;
+    const int nv_last = n_packed_b - (nt_seq - 1) * kTile;
+    auto tail_fix = [&](uint8_t *slot, int tile) -> int {
+        if constexpr (PAGED) {
+            if (tile == nt_seq - 1 && nv_last < kTile) {
+                if (lane >= nv_last && lane < kTile) {
+                    *reinterpret_cast<u32x4 *>(slot + G::KSZ + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4 *>(slot + G::VSZ + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+                }
+                lds_fence();
+                return nv_last;
+            }
+        }
+        return kTile;
+    };
 
     // key-channel norms of this row's channels 8*(lane%16)..+7 when q is to be multiplied
     // by them (loaded first, so they are older than every load waited for below)
@@ -352,8 +403,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
     uint8_t *ring = &sm.ring[wave][0][0];
 #pragma unroll
     for (int k = 0; k < RING; ++k)
-        if (k < nt_w) issue_tile<BITS>(rk, rv, ring + k * G::BYTES, my_lo + k * kWaves, lane,
-                                       a.block_bytes, a.sz_off);
+        if (k < nt_w) issue(ring + k * G::BYTES, my_lo + k * kWaves);
     wait_behind<BITS>(nt_w < RING ? nt_w : RING);     // q, issued before the tiles
     if (a.qnorm) {
         // q' = fp16(q * norm) per channel: lane (r, n) rescales the 16 bytes it loaded
@@ -427,26 +477,26 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
         PVIn cur;
         float alpha;
         bool resc;
-        stage_a_packed<BITS>(ring, pbuf, aq, qs, qinit, a.sm_log2, M, n, r, st, cur, alpha, resc);
+        const int nv0 = tail_fix(ring, my_lo);
+        stage_a_packed<BITS, PAGED>(ring, pbuf, aq, qs, qinit, a.sm_log2, M, n, r, st, cur, alpha,
+                                    resc, nv0);
         wait_lgkm0();                                    // slot 0 read, p of tile 0 written
-        if (RING < nt_w)
-            issue_tile<BITS>(rk, rv, ring, my_lo + RING * kWaves, lane, a.block_bytes, a.sz_off);
+        if (RING < nt_w) issue(ring, my_lo + RING * kWaves);
         // one pipeline step: stage A of tile k+1 (into `nxt`) next to stage B of tile k
         auto step = [&](int k, const PVIn &cur, PVIn &nxt) {
             // tile k+1 in LDS; the tiles up to k+RING may still be in flight
             wait_behind<BITS>(nt_w - 2 - k < RING - 1 ? nt_w - 2 - k : RING - 1);
             set_prio(nt_w - k);
             const int s1 = (k + 1) % RING;
+            const int nv = tail_fix(ring + s1 * G::BYTES, my_lo + (k + 1) * kWaves);
             float p8[8];
             load_p8(pbuf + (k & 1) * pstride, n, r, p8);
-            stage_a_packed<BITS>(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, aq, qs,
-                                 qinit, a.sm_log2, M, n, r, st, nxt, alpha, resc);
+            stage_a_packed<BITS, PAGED>(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, aq,
+                                        qs, qinit, a.sm_log2, M, n, r, st, nxt, alpha, resc, nv);
             stage_b_packed<BITS>(p8, cur, M, st);
             if (resc) rescale_pv(st, alpha);             // tile k's PV is in; tile k+1 moved m
             wait_lgkm0();                                // slot k+1 read, p of tile k+1 written
-            if (k + 1 + RING < nt_w)
-                issue_tile<BITS>(rk, rv, ring + s1 * G::BYTES, my_lo + (k + 1 + RING) * kWaves,
-                                 lane, a.block_bytes, a.sz_off);
+            if (k + 1 + RING < nt_w) issue(ring + s1 * G::BYTES, my_lo + (k + 1 + RING) * kWaves);
         };
         auto last = [&](int k, const PVIn &cur) {
             float p8[8];
@@ -474,13 +524,13 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
     if (with_res) {
         const uint16_t *kr = a.kres + row * a.res_cap * kHeadDim;
         const uint16_t *vr = a.vres + row * a.res_cap * kHeadDim;
-        const int n_rt = (a.n_res + kTile - 1) / kTile;
+        const int n_rt = (n_res_b + kTile - 1) / kTile;
         for (int rt = wave; rt < n_rt; rt += kWaves) {
             float lg[2], zv[2][4];
 #pragma unroll
             for (int u = 0; u < 2; ++u) {
                 const int ts = rt * kTile + 16 * u + n;
-                const int tc = ts < a.n_res ? ts : a.n_res - 1;
+                const int tc = ts < n_res_b ? ts : n_res_b - 1;
                 const uint16_t *kt = kr + (int64_t)tc * kHeadDim + 32 * r;
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -488,7 +538,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
                     acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(
                         aq[o], perm_octet_f16(*reinterpret_cast<const u32x4 *>(kt + 8 * o)), acc, 0, 0, 0);
                 const float s = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-                lg[u] = ts < a.n_res ? s * a.sm_log2 : -INFINITY;
+                lg[u] = ts < n_res_b ? s * a.sm_log2 : -INFINITY;
 #pragma unroll
                 for (int g = 0; g < 4; ++g) zv[u][g] = 0.0f;
             }
@@ -496,7 +546,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a)
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int ts = rt * kTile + 4 * e + r;
-                const int tc = ts < a.n_res ? ts : a.n_res - 1;
+                const int tc = ts < n_res_b ? ts : n_res_b - 1;
                 vt[e] = *reinterpret_cast<const u32x4 *>(vr + (int64_t)tc * kHeadDim + 8 * n);
             }
             half2_t vpair[4][8];
@@ -687,11 +737,12 @@ inline int ring_depth(int64_t workgroups, int bits)
     return KVQ_RING;
 }
 
-template <int BITS, int NH, int R>
-hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream)
+template <int BITS, int NH, int R, bool PAGED = false>
+hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream, const int32_t *tbl = nullptr)
 {
     constexpr int W = KVQ_WAVES;
-    hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W>), grid, dim3(64 * W), 0, stream, a);
+    hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W, PAGED>), grid, dim3(64 * W), 0, stream, a,
+                       tbl, a.state);
     return hipGetLastError();
 }
 
@@ -718,6 +769,32 @@ hipError_t launch_bits(const DecArgs &a, int nh, int64_t rows, int chunks, hipSt
     case 2: return launch_t<BITS, 2>(a, rows, chunks, stream);
     case 3: return launch_t<BITS, 3>(a, rows, chunks, stream);
     case 4: return launch_t<BITS, 4>(a, rows, chunks, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// paged cache: the default ring depth only
+template <int BITS>
+hipError_t launch_paged_bits(const DecArgs &a, const int32_t *tbl, int nh, int64_t rows,
+                             int chunks, hipStream_t stream)
+{
+    const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
+    switch (nh) {
+    case 1: return launch_r<BITS, 1, KVQ_RING, true>(a, grid, stream, tbl);
+    case 2: return launch_r<BITS, 2, KVQ_RING, true>(a, grid, stream, tbl);
+    case 3: return launch_r<BITS, 3, KVQ_RING, true>(a, grid, stream, tbl);
+    case 4: return launch_r<BITS, 4, KVQ_RING, true>(a, grid, stream, tbl);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_paged_nh(const DecArgs &a, const int32_t *tbl, int bits, int nh, int64_t rows,
+                           int chunks, hipStream_t stream)
+{
+    switch (bits) {
+    case 2: return launch_paged_bits<2>(a, tbl, nh, rows, chunks, stream);
+    case 3: return launch_paged_bits<3>(a, tbl, nh, rows, chunks, stream);
+    case 4: return launch_paged_bits<4>(a, tbl, nh, rows, chunks, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -761,6 +838,28 @@ hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream)
     if (tail > 0) {
         a.head_base = full * 4;
         e = launch_f16_heads(a, tail, rows, 1, stream);
+    }
+    return e;
+}
+
+hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream)
+{
+    DecArgs a = make_dec_args(p);
+    a.row_stride = 0;
+    a.row_bytes = 0;
+    a.n_packed = 0;     // per sequence, from the state
+    a.n_res = 0;
+    const int64_t rows = (int64_t)p.B * p.Hkv;
+    const int full = a.gq / 4, tail = a.gq % 4;
+    hipError_t e = hipSuccess;
+    if (full > 0) {
+        a.head_base = 0;
+        e = launch_paged_nh(a, p.tbl, p.bits, 4, rows, full, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) {
+        a.head_base = full * 4;
+        e = launch_paged_nh(a, p.tbl, p.bits, tail, rows, 1, stream);
     }
     return e;
 }

@@ -32,6 +32,11 @@ struct DecArgs {
     float *part_o, *part_lse;
     int32_t block_bytes, sz_off;
     const float *qnorm;          // key-channel norms [rows][128] q is multiplied by, or null
+    // paged cache (kp / vp are then the pools): block e of sequence b at
+    // pool + tbl[b][e] * block_stride + kvh * head_stride; lengths from state[b][0..1]
+    int32_t max_blocks;
+    int64_t pool_blocks, block_stride, head_stride;
+    const int32_t *state;
 };
 
 __device__ __forceinline__ void lds_fence()
@@ -71,16 +76,14 @@ __device__ __forceinline__ void dma(__amdgpu_buffer_rsrc_t r, uint8_t *lds, uint
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)lds, 16, voff, 0, 0, 0);
 }
 
-// Ask for packed tile `tile` (32 tokens) of this row: K and V codes and scale/zero.
+// Ask for the 32 tokens tb0 .. tb0+31 of the packed block at byte offset `blk` of the
+// K and V buffer resources: their codes and scale/zero.
 template <int BITS>
-__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
-                                           uint8_t *slot, int tile, int lane, int block_bytes,
-                                           int sz_off)
+__device__ __forceinline__ void issue_tile_at(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                              uint8_t *slot, uint32_t blk, int tb0, int lane,
+                                              int sz_off)
 {
     using G = TileGeom<BITS>;
-    const int tok0 = tile * kTile;
-    const uint32_t blk = (uint32_t)(tok0 >> 7) * (uint32_t)block_bytes;
-    const int tb0 = tok0 & 127;
     const uint32_t c0 = blk + tb0 * G::TOKB;
     if (BITS == 3) {          // 1536 B = 64 lanes x 16 B + 32 lanes x 16 B
         dma(rk, slot, c0 + lane * 16, 16);
@@ -101,6 +104,17 @@ __device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_b
         dma(rk, slot + G::KSZ, s0, 16);
         dma(rv, slot + G::VSZ, s0, 16);
     }
+}
+
+// Ask for packed tile `tile` (32 tokens) of a contiguous row.
+template <int BITS>
+__device__ __forceinline__ void issue_tile(__amdgpu_buffer_rsrc_t rk, __amdgpu_buffer_rsrc_t rv,
+                                           uint8_t *slot, int tile, int lane, int block_bytes,
+                                           int sz_off)
+{
+    const int tok0 = tile * kTile;
+    issue_tile_at<BITS>(rk, rv, slot, (uint32_t)(tok0 >> 7) * (uint32_t)block_bytes, tok0 & 127,
+                        lane, sz_off);
 }
 
 // s_waitcnt vmcnt(n) (gfx9 encoding; expcnt and lgkmcnt left at their maxima)
@@ -244,6 +258,11 @@ inline DecArgs make_dec_args(const DecodeParams &p)
     a.block_bytes = p.block_bytes;
     a.sz_off = p.sz_off;
     a.qnorm = p.qnorm;
+    a.max_blocks = p.max_blocks;
+    a.pool_blocks = p.pool_blocks;
+    a.block_stride = p.block_stride;
+    a.head_stride = p.head_stride;
+    a.state = p.state;
     a.row_bytes = (int32_t)((int64_t)(p.n_packed / kBlockTokens) * p.block_bytes);
     return a;
 }
@@ -264,6 +283,26 @@ __device__ __forceinline__ void split_range(const DecArgs &a, int split, int &tl
         with_res = !a.res_alone && split == a.S - 1;
     }
     with_res = with_res && a.n_res > 0;
+}
+
+// The same rule for one sequence of a paged cache with its own lengths: NT = ceil(n / 32)
+// tiles, the last one possibly partial.
+__device__ __forceinline__ void split_range_seq(const DecArgs &a, int split, int n_packed,
+                                                int n_res, int &tlo, int &thi, bool &with_res)
+{
+    const int NT = (n_packed + kTile - 1) / kTile;
+    const bool res_alone = a.S > 1 && n_res > 0;
+    const int Sp = res_alone ? a.S - 1 : a.S;
+    tlo = 0;
+    thi = 0;
+    if (res_alone && split == a.S - 1) {
+        with_res = true;
+    } else {
+        tlo = (int)((int64_t)split * NT / Sp);
+        thi = (int)((int64_t)(split + 1) * NT / Sp);
+        with_res = !res_alone && split == a.S - 1;
+    }
+    with_res = with_res && n_res > 0;
 }
 
 }  // namespace

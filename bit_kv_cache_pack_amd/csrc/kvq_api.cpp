@@ -225,6 +225,149 @@ kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res
         slot, stream));
 }
 
+}  // extern "C"
+
+namespace {
+
+// Validate a paged pool's geometry and fill the launcher's description of it.
+kvq_status check_pool(const kvq_format *fmt, int32_t Hkv, int64_t pool_blocks,
+                      int64_t block_stride, int64_t head_stride, const int32_t *tbl,
+                      int32_t max_blocks, kvq::PagedPool &pp)
+{
+    if (!tbl) return KVQ_ERR_NULL;
+    if (pool_blocks < 1 || max_blocks < 1 || block_stride < 1 || head_stride < 1)
+        return KVQ_ERR_SHAPE;
+    if ((int64_t)max_blocks * 128 > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (block_stride % 64 != 0 || head_stride % 64 != 0) return KVQ_ERR_ALIGN;
+    const int64_t bb = kvq_block_bytes(fmt);
+    // blocks of one head side by side ([blocks][Hkv][bb]) or heads side by side
+    // ([Hkv][blocks][bb]); anything else could overlap
+    const bool by_block = head_stride >= bb && block_stride / Hkv >= head_stride;
+    const bool by_head = block_stride >= bb && head_stride / pool_blocks >= block_stride;
+    if (!by_block && !by_head) return KVQ_ERR_SHAPE;
+    pp.bits = fmt->bits;
+    pp.hybrid = fmt->hybrid;
+    pp.pool_blocks = pool_blocks;
+    pp.block_stride = block_stride;
+    pp.head_stride = head_stride;
+    pp.tbl = tbl;
+    pp.max_blocks = max_blocks;
+    pp.block_bytes = (int32_t)bb;
+    pp.sz_off = (int32_t)kvq_sz_offset(fmt);
+    pp.flag_off = (int32_t)kvq_flag_offset(fmt);
+    return KVQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_pack_tokens_paged(const kvq_format *fmt, const void *src_fp16, int32_t B,
+                                 int32_t Hkv, int64_t src_row_stride, int64_t src_tok_stride,
+                                 const int32_t *count, const int32_t *start, int32_t max_count,
+                                 void *pool, int64_t pool_blocks, int64_t block_stride_bytes,
+                                 int64_t head_stride_bytes, const int32_t *block_table,
+                                 int32_t max_blocks, hipStream_t stream)
+{
+    kvq_status st = check_format(fmt);
+    if (st != KVQ_OK) return st;
+    if (!src_fp16 || !count || !start || !pool) return KVQ_ERR_NULL;
+    if (B < 1 || Hkv < 1 || max_count < 0) return KVQ_ERR_SHAPE;
+    if (src_row_stride < 0 || src_tok_stride < fmt->head_dim) return KVQ_ERR_SHAPE;
+    if (src_row_stride % 8 != 0 || src_tok_stride % 8 != 0) return KVQ_ERR_ALIGN;
+    if (!aligned64(src_fp16) || !aligned64(pool)) return KVQ_ERR_ALIGN;
+    kvq::PagedPool pp{};
+    st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
+                    max_blocks, pp);
+    if (st != KVQ_OK) return st;
+    if ((int64_t)B * Hkv * ((max_count + 63) / 64) > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    return launched(kvq::launch_pack_tokens_paged(
+        pp, static_cast<const uint16_t *>(src_fp16), B, Hkv, src_row_stride, src_tok_stride, count,
+        start, max_count, static_cast<uint8_t *>(pool), stream));
+}
+
+kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void *v_new,
+                            void *k_res, void *v_res, int32_t res_capacity, int32_t n_sink,
+                            void *k_pool, void *v_pool, int64_t pool_blocks,
+                            int64_t block_stride_bytes, int64_t head_stride_bytes,
+                            const int32_t *block_table, int32_t max_blocks, kvq_seq_state *state,
+                            int32_t B, int32_t Hkv, hipStream_t stream)
+{
+    kvq_status st = check_format(fmt);
+    if (st != KVQ_OK) return st;
+    if (!k_new || !v_new || !k_res || !v_res || !k_pool || !v_pool || !state) return KVQ_ERR_NULL;
+    if (B < 1 || Hkv < 1 || res_capacity < 1 || n_sink < 0 || n_sink >= res_capacity)
+        return KVQ_ERR_SHAPE;
+    if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (!aligned64(k_new) || !aligned64(v_new) || !aligned64(k_res) || !aligned64(v_res) ||
+        !aligned64(k_pool) || !aligned64(v_pool) || !aligned64(state))
+        return KVQ_ERR_ALIGN;
+    kvq::PagedPool pp{};
+    st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
+                    max_blocks, pp);
+    if (st != KVQ_OK) return st;
+    return launched(kvq::launch_append_evict(
+        pp, static_cast<const uint16_t *>(k_new), static_cast<const uint16_t *>(v_new),
+        static_cast<uint16_t *>(k_res), static_cast<uint16_t *>(v_res), res_capacity, n_sink,
+        static_cast<uint8_t *>(k_pool), static_cast<uint8_t *>(v_pool),
+        reinterpret_cast<int32_t *>(state), B, Hkv, stream));
+}
+
+kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                      int32_t Hq, int32_t Hkv, const void *k_pool,
+                                      const void *v_pool, int64_t pool_blocks,
+                                      int64_t block_stride_bytes, int64_t head_stride_bytes,
+                                      const int32_t *block_table, int32_t max_blocks,
+                                      const kvq_seq_state *state, const void *k_res_fp16,
+                                      const void *v_res_fp16, int32_t res_capacity,
+                                      float sm_scale, int32_t num_splits, float *part_o,
+                                      float *part_lse, hipStream_t stream)
+{
+    kvq_status st = check_format(fmt);
+    if (st != KVQ_OK) return st;
+    if (!q_fp16 || !k_pool || !v_pool || !state || !k_res_fp16 || !v_res_fp16 || !part_o ||
+        !part_lse)
+        return KVQ_ERR_NULL;
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || res_capacity < 1) return KVQ_ERR_SHAPE;
+    if (num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
+    if (!isfinite(sm_scale)) return KVQ_ERR_SHAPE;
+    if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
+    if ((int64_t)B * Hq * fmt->head_dim * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned64(q_fp16) || !aligned64(k_pool) || !aligned64(v_pool) || !aligned64(state) ||
+        !aligned64(k_res_fp16) || !aligned64(v_res_fp16) || !aligned64(part_o) ||
+        !aligned64(part_lse))
+        return KVQ_ERR_ALIGN;
+    kvq::PagedPool pp{};
+    st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
+                    max_blocks, pp);
+    if (st != KVQ_OK) return st;
+    kvq::DecodeParams p{};
+    p.q = static_cast<const uint16_t *>(q_fp16);
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.kp = static_cast<const uint8_t *>(k_pool);
+    p.vp = static_cast<const uint8_t *>(v_pool);
+    p.kres = static_cast<const uint16_t *>(k_res_fp16);
+    p.vres = static_cast<const uint16_t *>(v_res_fp16);
+    p.res_cap = res_capacity;
+    p.sm_scale = sm_scale;
+    p.num_splits = num_splits;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    p.bits = fmt->bits;
+    p.block_bytes = pp.block_bytes;
+    p.sz_off = pp.sz_off;
+    p.tbl = block_table;
+    p.max_blocks = max_blocks;
+    p.pool_blocks = pool_blocks;
+    p.block_stride = block_stride_bytes;
+    p.head_stride = head_stride_bytes;
+    p.state = reinterpret_cast<const int32_t *>(state);
+    return launched(kvq::launch_decode_paged(p, stream));
+}
+
 kvq_status kvq_key_norm(const void *k_fp16, int64_t n_rows, int32_t n_tokens,
                         int64_t row_stride, int64_t tok_stride, int32_t head_dim, float *norm,
                         hipStream_t stream)

@@ -26,10 +26,16 @@ struct DecodeParams {
     float *part_o, *part_lse;
     int32_t bits, block_bytes, sz_off;
     const float *qnorm;   // key-channel norms [B*Hkv][128] that q is multiplied by, or null
+    // paged cache only (kp / vp are the pools; n_packed / n_res come from state per sequence)
+    const int32_t *tbl;
+    int32_t max_blocks;
+    int64_t pool_blocks, block_stride, head_stride;
+    const int32_t *state;
 };
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
@@ -38,6 +44,25 @@ hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B,
 hipError_t launch_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
                          uint16_t *v_res, int32_t B, int32_t Hkv, int32_t res_cap, int32_t slot,
                          hipStream_t stream);
+
+// Geometry of a paged packed cache (pool of blocks addressed through a block table).
+struct PagedPool {
+    int32_t bits, hybrid;
+    int64_t pool_blocks, block_stride, head_stride;   // strides in bytes
+    const int32_t *tbl;                               // [B][max_blocks]
+    int32_t max_blocks;
+    int32_t block_bytes, sz_off, flag_off;
+};
+
+hipError_t launch_pack_tokens_paged(const PagedPool &pool, const uint16_t *src, int32_t B,
+                                    int32_t Hkv, int64_t src_row_stride, int64_t src_tok_stride,
+                                    const int32_t *count, const int32_t *start, int32_t max_count,
+                                    uint8_t *dst_pool, hipStream_t stream);
+
+hipError_t launch_append_evict(const PagedPool &pool, const uint16_t *k_new,
+                               const uint16_t *v_new, uint16_t *k_res, uint16_t *v_res,
+                               int32_t res_cap, int32_t n_sink, uint8_t *k_pool, uint8_t *v_pool,
+                               int32_t *state, int32_t B, int32_t Hkv, hipStream_t stream);
 
 hipError_t launch_key_norm(const uint16_t *k, int64_t n_rows, int32_t n_tokens,
                            int64_t row_stride, int64_t tok_stride, float *norm,

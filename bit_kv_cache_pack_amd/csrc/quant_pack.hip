@@ -16,27 +16,13 @@
 //
 // Every quantizer step is one IEEE binary32 operation (no contraction: see the pragma;
 // division is the correctly rounded one) so the bytes equal the CPU definition's.
-#include "kvq_device.h"
 #include "kvq_internal.h"
+#include "quant_common.h"
 
 #pragma clang fp contract(off)
 
 namespace kvq {
 namespace {
-
-template <int CTRL>
-__device__ __forceinline__ float quad_dpp(float v) { return dpp_f<CTRL>(v); }
-
-__device__ __forceinline__ float round_half_away_pos(float t)
-{
-    const float k = __builtin_truncf(t);
-    return (t - k >= 0.5f) ? k + 1.0f : k;
-}
-__device__ __forceinline__ float round_half_away(float t)
-{
-    const float r = round_half_away_pos(__builtin_fabsf(t));
-    return t < 0.0f ? -r : r;
-}
 
 struct QPArgs {
     const uint16_t *src;
@@ -50,9 +36,6 @@ struct QPArgs {
 template <int BITS, bool HYBRID>
 __global__ __launch_bounds__(256) void quant_pack_kernel(QPArgs a)
 {
-    constexpr int N = (1 << BITS) - 1;
-    constexpr int OFF = 1 << (BITS - 1);
-    constexpr int QS = OFF - 1;
     constexpr int GBYTES = 4 * BITS;   // bytes per packed group
 
     const int lane = threadIdx.x & 63;
@@ -84,86 +67,10 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(QPArgs a)
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
         const int tb = wave * 32 + it * 4 + tl;
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const half2_t h = as_h2(raw[it][i]);
-            x[2 * i] = (float)h.x;
-            x[2 * i + 1] = (float)h.y;
-        }
-        float mn = x[0], mx = x[0];
-#pragma unroll
-        for (int i = 1; i < 8; ++i) {
-            mn = fminf(mn, x[i]);
-            mx = fmaxf(mx, x[i]);
-        }
-        mn = fminf(mn, quad_dpp<0xB1>(mn));
-        mn = fminf(mn, quad_dpp<0x4E>(mn));
-        mx = fmaxf(mx, quad_dpp<0xB1>(mx));
-        mx = fmaxf(mx, quad_dpp<0x4E>(mx));
-        mn = mn + 0.0f;   // -0.0 -> +0.0
-        mx = mx + 0.0f;
-
-        // asymmetric candidate
-        const _Float16 sh = (_Float16)((mx - mn) / (float)N);
-        const _Float16 zh = (_Float16)mn;     // exact
-        const float s = (float)sh, z = (float)zh;
-        int code[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float c = 0.0f;
-            if (s != 0.0f) c = fminf(round_half_away_pos((x[i] - z) / s), (float)N);
-            code[i] = (int)c;
-        }
-        uint16_t out_s = __builtin_bit_cast(uint16_t, sh);
-        uint16_t out_z = __builtin_bit_cast(uint16_t, zh);
-        int flag = 1;
-
-        if (HYBRID) {
-            // symmetric candidate: signed grid k*ss, |k| <= QS, offset-binary codes
-            float am = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) am = fmaxf(am, __builtin_fabsf(x[i]));
-            am = fmaxf(am, quad_dpp<0xB1>(am));
-            am = fmaxf(am, quad_dpp<0x4E>(am));
-            const _Float16 ssh = (_Float16)(am / (float)QS);
-            const float ss = (float)ssh;
-            const float zs = -((float)OFF * ss) + 0.0f;
-            const bool eligible = __builtin_fabsf(zs) <= 65504.0f;
-            int scode[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                float k = 0.0f;
-                if (ss != 0.0f) k = fminf(fmaxf(round_half_away(x[i] / ss), -(float)QS), (float)QS);
-                scode[i] = OFF + (int)k;
-            }
-            // squared errors, balanced pairwise sum in channel order: 8 in-lane, then quad
-            float ea[8], es[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float da = x[i] - __builtin_fmaf((float)code[i], s, z);
-                const float ds = x[i] - __builtin_fmaf((float)scode[i], ss, zs);
-                ea[i] = da * da;
-                es[i] = ds * ds;
-            }
-            float sa = ((ea[0] + ea[1]) + (ea[2] + ea[3])) + ((ea[4] + ea[5]) + (ea[6] + ea[7]));
-            float se = ((es[0] + es[1]) + (es[2] + es[3])) + ((es[4] + es[5]) + (es[6] + es[7]));
-            sa = sa + quad_dpp<0xB1>(sa);
-            sa = sa + quad_dpp<0x4E>(sa);
-            se = se + quad_dpp<0xB1>(se);
-            se = se + quad_dpp<0x4E>(se);
-            if (eligible && se < sa) {
-                flag = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) code[i] = scode[i];
-                out_s = __builtin_bit_cast(uint16_t, ssh);
-                out_z = __builtin_bit_cast(uint16_t, (_Float16)zs);
-            }
-        }
-
-        uint32_t packed = 0;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) packed |= (uint32_t)code[i] << (BITS * i);
+        uint32_t packed;
+        uint16_t out_s, out_z;
+        int flag;
+        quantize_octet<BITS, HYBRID>(raw[it], packed, out_s, out_z, flag);
 
         uint8_t *gptr = dblk + (tb * kGroups + g) * GBYTES + j * BITS;
         if (BITS == 4) {

@@ -24,7 +24,8 @@ _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
 
 EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_knorm",
             "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
-            "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale")
+            "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale", "kvq_pack_tokens_paged",
+            "kvq_append_evict", "kvq_decode_attention_paged")
 
 
 class KVQError(RuntimeError):
@@ -112,6 +113,12 @@ def lib():
         L.kvq_key_norm.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp]
         L.kvq_channel_scale.argtypes = [vp, i64, i32, i64, i64, i32, vp, i64, i32, vp, i64, i64,
                                         vp]
+        L.kvq_pack_tokens_paged.argtypes = [fp, vp, i32, i32, i64, i64, vp, vp, i32, vp, i64,
+                                            i64, i64, vp, i32, vp]
+        L.kvq_append_evict.argtypes = [fp, vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, vp,
+                                       i32, vp, i32, i32, vp]
+        L.kvq_decode_attention_paged.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64, i64,
+                                                 vp, i32, vp, vp, vp, i32, f32, i32, vp, vp, vp]
         for n in EXPORTED:
             getattr(L, n).restype = C.c_int
         _lib = L
@@ -229,6 +236,46 @@ def kvq_channel_scale(x_fp16, n_rows: int, n_tokens: int, x_row_stride: int,
                                  head_dim, _ptr(norm), rows_per_norm, mode, _ptr(y_fp16),
                                  y_row_stride, y_tok_stride, _stream(stream, x_fp16))
     _check("kvq_channel_scale", st)
+
+
+def kvq_pack_tokens_paged(fmt: Format, src_fp16, B: int, Hkv: int, src_row_stride: int,
+                          src_tok_stride: int, count, start, max_count: int, pool,
+                          pool_blocks: int, block_stride_bytes: int, head_stride_bytes: int,
+                          block_table, max_blocks: int, stream=None):
+    f = fmt.c()
+    st = lib().kvq_pack_tokens_paged(C.byref(f), _ptr(src_fp16), B, Hkv, src_row_stride,
+                                     src_tok_stride, _ptr(count), _ptr(start), max_count,
+                                     _ptr(pool), pool_blocks, block_stride_bytes,
+                                     head_stride_bytes, _ptr(block_table), max_blocks,
+                                     _stream(stream, src_fp16, pool))
+    _check("kvq_pack_tokens_paged", st)
+
+
+def kvq_append_evict(fmt: Format, k_new, v_new, k_res, v_res, res_capacity: int, n_sink: int,
+                     k_pool, v_pool, pool_blocks: int, block_stride_bytes: int,
+                     head_stride_bytes: int, block_table, max_blocks: int, state, B: int,
+                     Hkv: int, stream=None):
+    f = fmt.c()
+    st = lib().kvq_append_evict(C.byref(f), _ptr(k_new), _ptr(v_new), _ptr(k_res), _ptr(v_res),
+                                res_capacity, n_sink, _ptr(k_pool), _ptr(v_pool), pool_blocks,
+                                block_stride_bytes, head_stride_bytes, _ptr(block_table),
+                                max_blocks, _ptr(state), B, Hkv, _stream(stream, k_new))
+    _check("kvq_append_evict", st)
+
+
+def kvq_decode_attention_paged(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_pool, v_pool,
+                               pool_blocks: int, block_stride_bytes: int,
+                               head_stride_bytes: int, block_table, max_blocks: int, state,
+                               k_res_fp16, v_res_fp16, res_capacity: int, sm_scale: float,
+                               num_splits: int, part_o, part_lse, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_paged(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_pool),
+                                          _ptr(v_pool), pool_blocks, block_stride_bytes,
+                                          head_stride_bytes, _ptr(block_table), max_blocks,
+                                          _ptr(state), _ptr(k_res_fp16), _ptr(v_res_fp16),
+                                          res_capacity, float(sm_scale), num_splits,
+                                          _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
+    _check("kvq_decode_attention_paged", st)
 
 
 def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:

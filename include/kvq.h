@@ -108,6 +108,15 @@ typedef enum { KVQ_OUT_F32 = 0, KVQ_OUT_F16 = 1 } kvq_out_dtype;
 
 typedef enum { KVQ_SCALE_DIVIDE = 0, KVQ_SCALE_MULTIPLY = 1 } kvq_scale_mode;
 
+/* Per-sequence state of a paged cache with a sliding window (see "Paged cache" below). */
+typedef struct {
+    int32_t n_packed;   /* tokens in the packed cache */
+    int32_t n_res;      /* window slots in use, 0..res_capacity (slots 0..n_res-1) */
+    int32_t next_slot;  /* once the window is full: the slot of its oldest recent token,
+                           in [n_sink, res_capacity); start it at n_sink */
+    int32_t reserved;   /* kept as it is */
+} kvq_seq_state;
+
 /* ---- size helpers (header-only) ---- */
 static inline int64_t kvq_align64(int64_t v) { return (v + 63) / 64 * 64; }
 static inline int64_t kvq_codes_bytes(const kvq_format *f)
@@ -328,6 +337,86 @@ kvq_status kvq_channel_scale(const void *x_fp16, int64_t n_rows, int32_t n_token
                              const float *norm, int64_t rows_per_norm, int32_t mode,
                              void *y_fp16, int64_t y_row_stride, int64_t y_tok_stride,
                              hipStream_t stream);
+
+/*
+ * ---------------------------------------------------------------------------------
+ * Paged cache, ragged lengths, per-token sliding window ([InnerQ] sec. 2.3: new tokens
+ * always enter the recent window, the oldest recent token is quantized into the main
+ * cache when the window is full, the sink window is fixed after prefill; [3-bit blog]
+ * sec. 6.1: the packed cache is kept in pages of a byte pool)
+ * ---------------------------------------------------------------------------------
+ * Packed blocks (the format above) live in a K pool and a V pool of pool_blocks blocks
+ * per kv-head. Packed token j of sequence b, kv-head h is token j % 128 of the block
+ *     pool + block_table[b][j / 128] * block_stride + h * head_stride      (bytes)
+ * block_table is int32 [B][max_blocks]. The strides are multiples of 64 and lay the pool
+ * out as [pool_blocks][Hkv][block_bytes] (head_stride >= block_bytes, block_stride >=
+ * Hkv * head_stride) or as [Hkv][pool_blocks][block_bytes] (block_stride >= block_bytes,
+ * head_stride >= pool_blocks * block_stride); KVQ_ERR_SHAPE otherwise.
+ * Each sequence has its own lengths, in a kvq_seq_state [B] array in device memory, and
+ * an fp16 window [B][Hkv][res_capacity][128] whose slots 0..n_sink-1 hold the sinks.
+ * Table entries, lengths and counts live on the device and are not checked on the host:
+ * a table entry outside [0, pool_blocks) or a position past the table makes the kernels
+ * skip that write (or read block 0 instead), and lengths are clamped to the table and the
+ * window, so bad device data gives wrong results but never an access outside the buffers.
+ */
+
+/*
+ * kvq_pack_tokens_paged -- quantize and pack tokens t = 0..count[b]-1 of every (b, h) row
+ * of src into packed positions start[b] + t of sequence b (prefill, or any bulk move into
+ * the paged cache); one token at a time, so a block may be filled in several calls. The
+ * bytes of each token equal those kvq_quantize_pack gives it; nothing else is written.
+ *   src_fp16        token t of row b*Hkv + h at src + (b*Hkv + h)*src_row_stride +
+ *                   t*src_tok_stride (elements, multiples of 8)
+ *   count, start    int32 [B] in device memory; max_count >= every count[b] (host bound
+ *                   for the grid; counts above it are cut to it)
+ *   pool            the K or the V pool
+ */
+kvq_status kvq_pack_tokens_paged(const kvq_format *fmt, const void *src_fp16, int32_t B,
+                                 int32_t Hkv, int64_t src_row_stride, int64_t src_tok_stride,
+                                 const int32_t *count, const int32_t *start, int32_t max_count,
+                                 void *pool, int64_t pool_blocks, int64_t block_stride_bytes,
+                                 int64_t head_stride_bytes, const int32_t *block_table,
+                                 int32_t max_blocks, hipStream_t stream);
+
+/*
+ * kvq_append_evict -- one decode step's cache update for every sequence b: if
+ * n_res < res_capacity the new token takes slot n_res (n_res += 1); otherwise the token in
+ * slot next_slot (the oldest recent one) is quantized into packed position n_packed
+ * (n_packed += 1), the new token takes that slot, and next_slot moves to the next slot,
+ * wrapping from res_capacity - 1 to n_sink. The state is updated on the device, so steps
+ * can be enqueued (or captured in a graph) without reading it back.
+ *   k_new, v_new    fp16 [B][Hkv][128]
+ *   k_res, v_res    fp16 [B][Hkv][res_capacity][128]
+ *   0 <= n_sink < res_capacity (the same on every call for a sequence)
+ * Calls on one stream apply in order; the decode of a step must follow its update.
+ */
+kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void *v_new,
+                            void *k_res, void *v_res, int32_t res_capacity, int32_t n_sink,
+                            void *k_pool, void *v_pool, int64_t pool_blocks,
+                            int64_t block_stride_bytes, int64_t head_stride_bytes,
+                            const int32_t *block_table, int32_t max_blocks, kvq_seq_state *state,
+                            int32_t B, int32_t Hkv, hipStream_t stream);
+
+/*
+ * kvq_decode_attention_paged -- the split-K partials of kvq_decode_attention for a paged
+ * cache: sequence b attends its own state[b].n_packed packed tokens (through the table;
+ * any number, not only multiples of 128) and its window slots 0..state[b].n_res-1.
+ * Split rule per sequence: NT = ceil(n_packed / 32) tiles (the last possibly partial);
+ * with num_splits S > 1 and n_res > 0 split S-1 holds the window and splits 0..S-2 share
+ * the tiles, otherwise all S share them and split S-1 also takes the window; split s of
+ * the Sp sharing splits gets tiles [s*NT/Sp, (s+1)*NT/Sp). Empty splits have lse = -inf
+ * and o = 0; every sequence needs at least one token for kvq_combine to be defined.
+ *   Other arguments, outputs and limits: as kvq_decode_attention.
+ */
+kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                      int32_t Hq, int32_t Hkv, const void *k_pool,
+                                      const void *v_pool, int64_t pool_blocks,
+                                      int64_t block_stride_bytes, int64_t head_stride_bytes,
+                                      const int32_t *block_table, int32_t max_blocks,
+                                      const kvq_seq_state *state, const void *k_res_fp16,
+                                      const void *v_res_fp16, int32_t res_capacity,
+                                      float sm_scale, int32_t num_splits, float *part_o,
+                                      float *part_lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -171,6 +171,97 @@ def make_inputs(wl: Workload | str, seed: int | None = None, L: int | None = Non
     return Inputs(wl, q, k, v, rng, meta)
 
 
+@dataclass(frozen=True)
+class PagedWorkload:
+    """Serving-shaped batch for the paged cache: B sequences of ragged lengths drawn
+    uniformly from [L_min, L_max] (each sequence: min(L, res_cap) tokens in its fp16
+    window, the rest packed), blocks of all sequences scattered over one pool."""
+    name: str
+    B: int
+    Hq: int
+    Hkv: int
+    L_min: int
+    L_max: int
+    bits: int
+    hybrid: bool = False
+    res_cap: int = RES_CAP
+    spare_blocks: int = 16        # pool blocks no sequence uses
+    seed: int = 0
+    description: str = ""
+    head_dim: int = HEAD_DIM
+
+    @property
+    def gq(self) -> int:
+        return self.Hq // self.Hkv
+
+    def kv_bytes_per_token_head(self) -> int:
+        ng = self.head_dim // 32
+        return 2 * (self.head_dim * self.bits // 8 + ng * 4)
+
+
+PAGED_WORKLOADS = {
+    "paged_ragged_b16": PagedWorkload(
+        "paged_ragged_b16", B=16, Hq=32, Hkv=8, L_min=1024, L_max=32768, bits=4,
+        description="16 sequences, L ~ U[1K, 32K], 32q/8kv, 4-bit asym, 128-slot fp16 windows, "
+                    "blocks scattered over one pool"),
+}
+
+
+@dataclass
+class PagedInputs:
+    wl: PagedWorkload
+    q: np.ndarray               # fp16 [B][Hq][d]
+    k_src: list                 # per sequence: fp16 [Hkv][n_packed_b][d] (packed part)
+    v_src: list
+    k_res: np.ndarray           # fp16 [B][Hkv][res_cap][d]
+    v_res: np.ndarray
+    n_packed: np.ndarray        # int32 [B]
+    n_res: np.ndarray           # int32 [B]
+    table: np.ndarray           # int32 [B][max_blocks], -1 where unused
+    n_pool_blocks: int
+
+    def step_bytes(self) -> int:
+        """Codes + fp16 scale/zero of every packed token and the fp16 window tokens read by
+        one decode step over the whole batch."""
+        wl = self.wl
+        return wl.Hkv * (int(self.n_packed.sum()) * wl.kv_bytes_per_token_head()
+                         + int(self.n_res.sum()) * 2 * wl.head_dim * 2)
+
+
+def make_paged_inputs(wl: PagedWorkload | str, seed: int | None = None) -> PagedInputs:
+    """Lengths first, then per sequence K and V of its packed part and its window, then q,
+    then the pool placement (a random permutation of the pool's blocks)."""
+    if isinstance(wl, str):
+        wl = PAGED_WORKLOADS[wl]
+    rng = np.random.default_rng(wl.seed if seed is None else seed)
+    d = wl.head_dim
+    L = rng.integers(wl.L_min, wl.L_max + 1, wl.B)
+    n_res = np.minimum(L, wl.res_cap).astype(np.int32)
+    n_packed = (L - n_res).astype(np.int32)
+    k_src, v_src = [], []
+    k_res = np.zeros((wl.B, wl.Hkv, wl.res_cap, d), np.float16)
+    v_res = np.zeros_like(k_res)
+    for b in range(wl.B):
+        k_src.append(rng.standard_normal((wl.Hkv, int(n_packed[b]), d), dtype=np.float32)
+                     .astype(np.float16))
+        v_src.append(rng.standard_normal((wl.Hkv, int(n_packed[b]), d), dtype=np.float32)
+                     .astype(np.float16))
+        k_res[b, :, :n_res[b]] = rng.standard_normal((wl.Hkv, int(n_res[b]), d),
+                                                     dtype=np.float32).astype(np.float16)
+        v_res[b, :, :n_res[b]] = rng.standard_normal((wl.Hkv, int(n_res[b]), d),
+                                                     dtype=np.float32).astype(np.float16)
+    q = rng.standard_normal((wl.B, wl.Hq, d), dtype=np.float32).astype(np.float16)
+    nblk = [(int(n) + 127) // 128 for n in n_packed]
+    n_pool = sum(nblk) + wl.spare_blocks
+    perm = rng.permutation(n_pool)
+    table = np.full((wl.B, max(max(nblk), 1)), -1, np.int32)
+    k = 0
+    for b, nb in enumerate(nblk):
+        table[b, :nb] = perm[k:k + nb]
+        k += nb
+    return PagedInputs(wl, q, k_src, v_src, k_res, v_res, n_packed, n_res, table, n_pool)
+
+
 def append_step_inputs(rng: np.random.Generator, wl: Workload):
     """One decode step of the append workload: new K, V token per (batch, kv-head) and q."""
     d = wl.head_dim

@@ -245,3 +245,105 @@ def _cs(x=A, rows=2, T=300, xrs=512 * 128, xts=128, hd=128, norm=A, rpn=1, mode=
 ])
 def test_channel_scale_rejects(kw, status):
     assert _cs(**kw) == status
+
+
+BB4 = 10240          # 4-bit block bytes
+
+
+def _pool_kw(**kw):
+    d = dict(pool_blocks=10, bs=2 * BB4, hs=BB4, tbl=A, maxb=4)
+    d.update(kw)
+    return d
+
+
+def _ptp(fmt=None, src=A, B=2, Hkv=2, rs=256 * 128, ts=128, cnt=A, st=A, maxc=256, pool=A, **kw):
+    f = _fmt() if fmt is None else fmt
+    p = _pool_kw(**kw)
+    return K.lib().kvq_pack_tokens_paged(C.byref(f), src, B, Hkv, rs, ts, cnt, st, maxc, pool,
+                                         p["pool_blocks"], p["bs"], p["hs"], p["tbl"], p["maxb"],
+                                         None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=_fmt(bits=1)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(src=None), K.KVQ_ERR_NULL),
+    (dict(cnt=None), K.KVQ_ERR_NULL),
+    (dict(st=None), K.KVQ_ERR_NULL),
+    (dict(pool=None), K.KVQ_ERR_NULL),
+    (dict(tbl=None), K.KVQ_ERR_NULL),
+    (dict(B=0), K.KVQ_ERR_SHAPE),
+    (dict(maxc=-1), K.KVQ_ERR_SHAPE),
+    (dict(ts=64), K.KVQ_ERR_SHAPE),
+    (dict(ts=132), K.KVQ_ERR_ALIGN),
+    (dict(src=MIS), K.KVQ_ERR_ALIGN),
+    (dict(pool=MIS), K.KVQ_ERR_ALIGN),
+    (dict(pool_blocks=0), K.KVQ_ERR_SHAPE),
+    (dict(maxb=0), K.KVQ_ERR_SHAPE),
+    (dict(bs=2 * BB4 + 32), K.KVQ_ERR_ALIGN),
+    (dict(hs=BB4 - 64), K.KVQ_ERR_SHAPE),             # heads of a block overlap
+    (dict(bs=BB4, hs=BB4), K.KVQ_ERR_SHAPE),          # blocks overlap the next head
+    (dict(maxb=1 << 24), K.KVQ_ERR_SHAPE),
+])
+def test_pack_tokens_paged_rejects(kw, status):
+    assert _ptp(**kw) == status
+
+
+def test_pack_tokens_paged_accepts_both_pool_layouts():
+    # [blocks][Hkv][bb] and [Hkv][blocks][bb]; max_count 0 launches nothing
+    assert _ptp(maxc=0) == K.KVQ_OK
+    assert _ptp(maxc=0, bs=BB4, hs=10 * BB4) == K.KVQ_OK
+
+
+def _ae(fmt=None, kn=A, vn=A, kr=A, vr=A, cap=128, sink=4, kp=A, vp=A, state=A, B=2, Hkv=2, **kw):
+    f = _fmt() if fmt is None else fmt
+    p = _pool_kw(**kw)
+    return K.lib().kvq_append_evict(C.byref(f), kn, vn, kr, vr, cap, sink, kp, vp,
+                                    p["pool_blocks"], p["bs"], p["hs"], p["tbl"], p["maxb"],
+                                    state, B, Hkv, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), K.KVQ_ERR_NULL),
+    (dict(vp=None), K.KVQ_ERR_NULL),
+    (dict(state=None), K.KVQ_ERR_NULL),
+    (dict(tbl=None), K.KVQ_ERR_NULL),
+    (dict(cap=0), K.KVQ_ERR_SHAPE),
+    (dict(sink=128), K.KVQ_ERR_SHAPE),
+    (dict(sink=-1), K.KVQ_ERR_SHAPE),
+    (dict(B=0), K.KVQ_ERR_SHAPE),
+    (dict(state=A + 16), K.KVQ_ERR_ALIGN),
+    (dict(kr=MIS), K.KVQ_ERR_ALIGN),
+    (dict(hs=64), K.KVQ_ERR_SHAPE),
+    (dict(fmt=_fmt(group=16)), K.KVQ_ERR_UNSUPPORTED),
+])
+def test_append_evict_rejects(kw, status):
+    assert _ae(**kw) == status
+
+
+def _dp(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, kr=A, vr=A, cap=128, sm=0.088,
+        S=4, po=A, pl=A, **kw):
+    f = _fmt() if fmt is None else fmt
+    p = _pool_kw(**kw)
+    return K.lib().kvq_decode_attention_paged(C.byref(f), q, B, Hq, Hkv, kp, vp,
+                                              p["pool_blocks"], p["bs"], p["hs"], p["tbl"],
+                                              p["maxb"], state, kr, vr, cap, sm, S, po, pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(state=None), K.KVQ_ERR_NULL),
+    (dict(kr=None), K.KVQ_ERR_NULL),
+    (dict(tbl=None), K.KVQ_ERR_NULL),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(cap=0), K.KVQ_ERR_SHAPE),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(sm=float("nan")), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(po=MIS), K.KVQ_ERR_ALIGN),
+    (dict(state=A + 16), K.KVQ_ERR_ALIGN),
+    (dict(bs=3 * BB4 + 16), K.KVQ_ERR_ALIGN),
+    (dict(pool_blocks=0), K.KVQ_ERR_SHAPE),
+    (dict(fmt=_fmt(bits=6)), K.KVQ_ERR_UNSUPPORTED),
+])
+def test_decode_paged_rejects(kw, status):
+    assert _dp(**kw) == status
