@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-fp16-baseline", action="store_true")
     ap.add_argument("--no-key-norm", action="store_true")
+    ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--paged-workload", default="paged_ragged_b16")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
     return ap.parse_args()
@@ -96,6 +98,91 @@ def cpu_baseline(wl, x, seconds: float):
             "ms_per_step": round(step_s * 1e3, 3),
             "sample": f"{reps} full decode steps of {wl.name} (all {wl.B * wl.Hq} heads, "
                       f"{wl.L} tokens; dequantize + fp64 softmax attention), {el:.1f} s"}
+
+
+def paged_bench(args, K, S, dev, stream, sptr, timed):
+    import numpy as np
+    import torch
+    pw = S.PAGED_WORKLOADS[args.paged_workload]
+    x = S.make_paged_inputs(pw)
+    fmt = K.Format(pw.bits, 128, pw.hybrid)
+    bb = fmt.block_bytes
+    B, Hkv, Hq, cap = pw.B, pw.Hkv, pw.Hq, pw.res_cap
+    # one spare block per sequence after its last one, so the timed steps (each appends a
+    # token to every sequence and evicts one into the packed cache) always have room
+    maxb = x.table.shape[1] + 1
+    tbl_np = np.full((B, maxb), -1, np.int32)
+    tbl_np[:, :maxb - 1] = x.table
+    for b in range(B):
+        tbl_np[b, (int(x.n_packed[b]) + 127) // 128] = x.n_pool_blocks + b
+    npool = x.n_pool_blocks + B
+    bs, hs = Hkv * bb, bb
+    tbl = torch.from_numpy(tbl_np).to(dev)
+    # packed cache built on the GPU, one sequence at a time
+    kpool = torch.zeros((npool, Hkv, bb), dtype=torch.uint8, device=dev)
+    vpool = torch.zeros_like(kpool)
+    for b in range(B):
+        n = int(x.n_packed[b])
+        if n == 0:
+            continue
+        cnt = torch.tensor([n], dtype=torch.int32, device=dev)
+        zero = torch.zeros(1, dtype=torch.int32, device=dev)
+        for src, pool in ((x.k_src[b], kpool), (x.v_src[b], vpool)):
+            sd = torch.from_numpy(np.ascontiguousarray(src)).to(dev)
+            K.kvq_pack_tokens_paged(fmt, sd, 1, Hkv, n * 128, 128, cnt, zero, n, pool, npool,
+                                    bs, hs, tbl[b:b + 1], maxb)
+            del sd
+    step_bytes = x.step_bytes()
+    copies = max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+    kr0 = torch.from_numpy(x.k_res).to(dev)
+    vr0 = torch.from_numpy(x.v_res).to(dev)
+    st0 = np.zeros((B, 4), np.int32)
+    st0[:, 0], st0[:, 1], st0[:, 2] = x.n_packed, x.n_res, 0
+    state0 = torch.from_numpy(st0).to(dev)
+    caches = [(kpool, vpool, kr0, vr0, state0)] + [
+        (kpool.clone(), vpool.clone(), kr0.clone(), vr0.clone(), state0.clone())
+        for _ in range(copies - 1)]
+    q = torch.from_numpy(x.q).to(dev)
+    S_ = K.suggest_splits_paged(int(x.n_packed.sum()), int(x.n_packed.max()), Hkv,
+                                torch.cuda.get_device_properties(dev).multi_processor_count)
+    po = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((B, Hq, S_), dtype=torch.float32, device=dev)
+    out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
+    kn = torch.zeros((B, Hkv, 128), dtype=torch.float16, device=dev)
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+
+    def decode(i, sp=sptr):
+        kp, vp, krd, vrd, st = caches[i % copies]
+        K.kvq_decode_attention_paged(fmt, q, B, Hq, Hkv, kp, vp, npool, bs, hs, tbl, maxb, st,
+                                     krd, vrd, cap, sm, S_, po, pl, stream=sp)
+
+    def update(i, sp=sptr):
+        kp, vp, krd, vrd, st = caches[i % copies]
+        K.kvq_append_evict(fmt, kn, kn, krd, vrd, cap, 0, kp, vp, npool, bs, hs, tbl, maxb, st,
+                           B, Hkv, stream=sp)
+
+    def step(i, sp=sptr):
+        update(i, sp)
+        decode(i, sp)
+        K.kvq_combine(po, pl, B, Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+    # every sequence grows by one packed token per update: at most 204 updates over >= 2
+    # cache copies stay within the spare block
+    steps = min(args.steps, 100)
+    step_ms = timed(step, steps, 2)
+    dec_ms = timed(decode, args.steps, 5)
+    upd_ms = timed(update, min(args.steps, 100), 2)
+    res = {"workload": pw.name, "B": B, "Hq": Hq, "Hkv": Hkv, "bits": pw.bits,
+           "lengths": [int(v) for v in (x.n_packed + x.n_res)], "splits": S_,
+           "cache_copies": copies, "step_bytes": step_bytes,
+           "us_per_step": round(step_ms * 1e3, 3),
+           "decode_kernel_us": round(dec_ms * 1e3, 3),
+           "append_evict_us": round(upd_ms * 1e3, 3),
+           "GB_per_s_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+           "GB_per_s_decode": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1),
+           "frac_decode": round(step_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    del caches, kpool, vpool
+    return res
 
 
 def main():
@@ -278,6 +365,14 @@ def main():
         del ksrc, kdst
     del kps_d
 
+    # paged cache: a serving-shaped batch of ragged sequences whose blocks are scattered
+    # over one pool. One step = kvq_append_evict (the new token of every sequence enters
+    # its window, evicting the oldest recent token into the packed cache) +
+    # kvq_decode_attention_paged + kvq_combine. Bytes = the step's algorithmic decode bytes.
+    paged = None
+    if not args.no_paged:
+        paged = paged_bench(args, K, S, dev, stream, sptr, timed)
+
     # flush (quantize the full 128-token window of every row, K and V) and append
     fl_reps = 50
     fsrc = [(c[2], c[3]) for c in caches]
@@ -347,6 +442,7 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes},
         "fp16_baseline": fp16,
         "key_norm": knorm,
+        "paged": paged,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (kvq_decode_attention)"},

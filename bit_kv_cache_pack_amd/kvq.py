@@ -285,3 +285,12 @@ def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
     want = (2 * cu_count + rows - 1) // rows
     cap = tiles // 8
     return int(max(1, min(256, min(want, cap))))
+
+
+def suggest_splits_paged(total_packed: int, max_packed: int, Hkv: int, cu_count: int = 256) -> int:
+    """Same rule as the header's kvq_suggest_splits_paged."""
+    if total_packed < 1 or max_packed < 1:
+        return 1
+    s = (4 * cu_count * max_packed + total_packed * Hkv - 1) // (total_packed * Hkv)
+    s = min(s, max_packed // 32 // 8)
+    return int(max(1, min(256, s)))

@@ -347,3 +347,12 @@ def _dp(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, kr=A, vr=A, cap=12
 ])
 def test_decode_paged_rejects(kw, status):
     assert _dp(**kw) == status
+
+
+def test_suggest_splits_paged_bounds():
+    assert K.suggest_splits_paged(0, 0, 8) == 1
+    # 16 sequences of 1.5K..32K tokens, 8 kv heads: 16 splits
+    assert K.suggest_splits_paged(270520, 31712, 8) == 16
+    for total, mx, hkv in [(32640, 32640, 8), (10 ** 7, 4096, 40), (100, 100, 1), (5000, 300, 2)]:
+        s = K.suggest_splits_paged(total, mx, hkv)
+        assert 1 <= s <= 256 and s <= max(1, mx // 256)

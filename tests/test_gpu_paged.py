@@ -322,7 +322,7 @@ def test_prefill_then_sliding_steps_then_decode(oracle_mod):
 @pytest.mark.slow
 def test_paged_decode_full_size_ragged(oracle_mod):
     """16 sequences of 1K..32K tokens, Llama-8B heads (32 q / 8 kv), 4-bit, the split count
-    the library suggests for the longest: every output against the oracle."""
+    the library suggests for ragged batches: every output against the oracle."""
     from gpu_common import assert_close
     O = oracle_mod
     wl = S.PAGED_WORKLOADS["paged_ragged_b16"]
@@ -330,7 +330,7 @@ def test_paged_decode_full_size_ragged(oracle_mod):
     fmt, ofmt = K.Format(wl.bits), O.Format(wl.bits)
     print(f"[decode_paged] full size {wl.name}", flush=True)
     c = _paged_from_inputs(O, ofmt, wl, x)
-    S_ = K.suggest_splits(1, wl.Hkv * wl.B, int(x.n_packed.max()), 256)
+    S_ = K.suggest_splits_paged(int(x.n_packed.sum()), int(x.n_packed.max()), wl.Hkv, 256)
     out, po, pl = _gpu_paged_decode(fmt, c, wl.B, wl.Hq, wl.Hkv, S_)
     ref = O.attention_paged(ofmt, c["q"], wl.Hkv, c["kpool"], c["vpool"], c["tbl"], c["state"],
                             c["kres"], c["vres"], sm=SM, block_stride=c["bs"], head_stride=c["hs"])
