@@ -23,7 +23,11 @@
  *   5. the split-K form of the same attention (per-split max / sum / normalised output)
  *      and the log-sum-exp merge of the splits, in fp64;
  *   6. key-channel normalization before quantization (InnerQ page, sec. 2.4): per-channel
- *      norm = sqrt(max |K|) over the prefill keys, keys divided by it, queries multiplied.
+ *      norm = sqrt(max |K|) over the prefill keys, keys divided by it, queries multiplied;
+ *   7. the paged cache with ragged lengths and the per-token sliding window (InnerQ page,
+ *      sec. 2.3; 3-bit blog page, sec. 6.1);
+ *   8. the outer-dimension (KIVI-style) grouping the InnerQ page compares against (sec. 1,
+ *      sec. 4.1): groups of 32 tokens per channel.
  *
  * Floating point: every quantizer step is one IEEE binary32 operation with round to
  * nearest even (build with -O2 -ffp-contract=off, never -ffast-math). Attention is fp64.
@@ -438,7 +442,10 @@ typedef struct {
     int S;                 /* number of splits (1 = plain attention) */
     double *out;           /* [B][Hq][d] when S == 0; part_o [B][Hq][S][d] otherwise */
     double *lse;           /* part_lse [B][Hq][S] */
+    int outer;             /* 1: blocks hold outer-dimension groups (see below) */
 } att_ctx;
+
+static void dequant_token_outer(const uint8_t *row, int bits, int head_dim, int64_t t, double *out);
 
 /* Token j of the sequence of (b, kvh): its key (which = 0) or value (which = 1) in fp64. */
 static void load_token(const att_ctx *c, int b, int kvh, int64_t j, int which, double *x)
@@ -446,7 +453,10 @@ static void load_token(const att_ctx *c, int b, int kvh, int64_t j, int which, d
     const int64_t row = (int64_t)b * c->Hkv + kvh;
     if (j < c->n_packed) {
         const uint8_t *base = which ? c->vp : c->kp;
-        dequant_token(base + row * c->row_stride, c->bits, c->head_dim, c->hybrid, j, x);
+        if (c->outer)
+            dequant_token_outer(base + row * c->row_stride, c->bits, c->head_dim, j, x);
+        else
+            dequant_token(base + row * c->row_stride, c->bits, c->head_dim, c->hybrid, j, x);
     } else {
         const int64_t slot = j - c->n_packed;
         const uint16_t *r = (which ? c->vres : c->kres) + (row * c->res_cap + slot) * c->head_dim;
@@ -549,7 +559,7 @@ void oq_attention(int bits, int head_dim, int hybrid, const uint16_t *q, int B, 
                   double *out, int n_threads)
 {
     att_ctx c = {bits, head_dim, hybrid, q, B, Hq, Hkv, kp, vp, row_stride, n_packed,
-                 kres, vres, res_cap, n_res, sm, 0, out, NULL};
+                 kres, vres, res_cap, n_res, sm, 0, out, NULL, 0};
     oq_parallel_for((int64_t)B * Hq, n_threads, att_head, &c);
 }
 
@@ -561,7 +571,7 @@ void oq_split_attention(int bits, int head_dim, int hybrid, const uint16_t *q, i
                         int n_threads)
 {
     att_ctx c = {bits, head_dim, hybrid, q, B, Hq, Hkv, kp, vp, row_stride, n_packed,
-                 kres, vres, res_cap, n_res, sm, S, part_o, part_lse};
+                 kres, vres, res_cap, n_res, sm, S, part_o, part_lse, 0};
     oq_parallel_for((int64_t)B * Hq, n_threads, att_head_split, &c);
 }
 
@@ -856,4 +866,97 @@ void oq_paged_split_range(int64_t n_packed, int64_t n_res, int S, int s, int64_t
                           int64_t *hi)
 {
     paged_split_range(n_packed, n_res, S, s, lo, hi);
+}
+
+/* ------------------------------------------------------------------------------------ */
+/* Outer-dimension grouping, the KIVI-style layout the InnerQ page sets against its own  */
+/* (sec. 1: the conventional scheme groups the cache along the sequence dimension, so    */
+/* the values of one token row belong to different groups and need their own scale and  */
+/* zero; sec. 4.1 times it as "KIVI (outer)"). Readings: a group is the 32 consecutive   */
+/* tokens 32*tg .. 32*tg+31 of a 128-token block in one channel, for K and for V; the    */
+/* quantizer is the same asymmetric one (no hybrid); codes keep the inner layout's        */
+/* positions (token t, channel c: word c/32 of token t, bits b*(c%32)), and the          */
+/* scale/zero region holds [4 token groups][head_dim channels]{fp16 scale, fp16 zero}    */
+/* (the same 2048 bytes at the same offset), so a block has the inner block's size.      */
+/* ------------------------------------------------------------------------------------ */
+
+int oq_quantize_pack_outer(int bits, int head_dim, const uint16_t *src, int64_t n_rows,
+                           int n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                           uint8_t *dst, int64_t dst_row_stride, int first_block)
+{
+    if (bits < 2 || bits > 4 || head_dim % OQ_GROUP || n_tokens % OQ_BLOCK)
+        return -1;
+    const int64_t bb = oq_block_bytes(bits, head_dim, 0);
+    const int ng = head_dim / OQ_GROUP;
+    const int64_t gbytes = OQ_GROUP * bits / 8;
+    uint8_t *codes = malloc((size_t)OQ_BLOCK * head_dim);
+    for (int64_t r = 0; r < n_rows; r++) {
+        for (int blk = 0; blk < n_tokens / OQ_BLOCK; blk++) {
+            uint8_t *out = dst + r * dst_row_stride + (int64_t)(first_block + blk) * bb;
+            memset(out, 0, (size_t)bb);
+            const uint16_t *sb = src + r * src_row_stride + (int64_t)blk * OQ_BLOCK * src_tok_stride;
+            for (int tg = 0; tg < OQ_BLOCK / OQ_GROUP; tg++) {
+                for (int c = 0; c < head_dim; c++) {
+                    uint16_t x[OQ_GROUP], sc, z;
+                    uint8_t cd[OQ_GROUP];
+                    for (int i = 0; i < OQ_GROUP; i++)
+                        x[i] = sb[(int64_t)(OQ_GROUP * tg + i) * src_tok_stride + c];
+                    oq_asym_candidate(x, bits, &sc, &z, cd);
+                    for (int i = 0; i < OQ_GROUP; i++)
+                        codes[(OQ_GROUP * tg + i) * head_dim + c] = cd[i];
+                    uint8_t *sz = out + oq_sz_offset(bits, head_dim) + ((int64_t)tg * head_dim + c) * 4;
+                    put_u16(sz, sc);
+                    put_u16(sz + 2, z);
+                }
+            }
+            for (int t = 0; t < OQ_BLOCK; t++)
+                for (int g = 0; g < ng; g++)
+                    oq_pack_codes(codes + t * head_dim + g * OQ_GROUP, bits,
+                                  out + (int64_t)t * ng * gbytes + g * gbytes);
+        }
+    }
+    free(codes);
+    return 0;
+}
+
+/* Token t of one outer-grouped packed row in fp64: x[c] = zero(tg, c) + code * scale(tg, c). */
+static void dequant_token_outer(const uint8_t *row, int bits, int head_dim, int64_t t, double *out)
+{
+    const int ng = head_dim / OQ_GROUP;
+    const int64_t gbytes = OQ_GROUP * bits / 8;
+    const uint8_t *blk = row + (t / OQ_BLOCK) * oq_block_bytes(bits, head_dim, 0);
+    const int tb = (int)(t % OQ_BLOCK);
+    const int tg = tb / OQ_GROUP;
+    for (int g = 0; g < ng; g++) {
+        uint8_t codes[OQ_GROUP];
+        oq_unpack_codes(blk + (int64_t)tb * ng * gbytes + g * gbytes, bits, codes);
+        for (int i = 0; i < OQ_GROUP; i++) {
+            const int c = g * OQ_GROUP + i;
+            const uint8_t *sz = blk + oq_sz_offset(bits, head_dim) + ((int64_t)tg * head_dim + c) * 4;
+            const double sc = (double)oq_f16_to_f32(get_u16(sz));
+            const double z = (double)oq_f16_to_f32(get_u16(sz + 2));
+            out[c] = z + (double)codes[i] * sc;
+        }
+    }
+}
+
+void oq_attention_outer(int bits, int head_dim, const uint16_t *q, int B, int Hq, int Hkv,
+                        const uint8_t *kp, const uint8_t *vp, int64_t row_stride, int n_packed,
+                        const uint16_t *kres, const uint16_t *vres, int res_cap, int n_res,
+                        double sm, double *out, int n_threads)
+{
+    att_ctx c = {bits, head_dim, 0, q, B, Hq, Hkv, kp, vp, row_stride, n_packed,
+                 kres, vres, res_cap, n_res, sm, 0, out, NULL, 1};
+    oq_parallel_for((int64_t)B * Hq, n_threads, att_head, &c);
+}
+
+void oq_split_attention_outer(int bits, int head_dim, const uint16_t *q, int B, int Hq, int Hkv,
+                              const uint8_t *kp, const uint8_t *vp, int64_t row_stride,
+                              int n_packed, const uint16_t *kres, const uint16_t *vres,
+                              int res_cap, int n_res, double sm, int S, double *part_o,
+                              double *part_lse, int n_threads)
+{
+    att_ctx c = {bits, head_dim, 0, q, B, Hq, Hkv, kp, vp, row_stride, n_packed,
+                 kres, vres, res_cap, n_res, sm, S, part_o, part_lse, 1};
+    oq_parallel_for((int64_t)B * Hq, n_threads, att_head_split, &c);
 }

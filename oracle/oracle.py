@@ -74,6 +74,11 @@ def _setup(L):
     L.oq_split_range.argtypes = [i32, i32, i32, i32, C.POINTER(i64), C.POINTER(i64)]
     L.oq_key_norm.argtypes = [vp, i64, i64, i64, i64, i32, vp]
     L.oq_channel_scale.argtypes = [vp, i64, i64, i64, i64, i32, vp, i64, i32, vp, i64, i64]
+    L.oq_quantize_pack_outer.argtypes = [i32, i32, vp, i64, i32, i64, i64, vp, i64, i32]
+    L.oq_quantize_pack_outer.restype = i32
+    L.oq_attention_outer.argtypes = L.oq_attention.argtypes[:2] + L.oq_attention.argtypes[3:]
+    L.oq_split_attention_outer.argtypes = (L.oq_split_attention.argtypes[:2] +
+                                           L.oq_split_attention.argtypes[3:])
     L.oq_pack_tokens_paged.argtypes = [i32, i32, i32, vp, i32, i32, i64, i64, vp, vp, vp, i64,
                                        i64, vp, i32]
     L.oq_append_evict.argtypes = [i32, i32, i32, vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, vp,
@@ -403,3 +408,48 @@ def paged_split_range(n_packed: int, n_res: int, S: int, s: int) -> tuple[int, i
     lo, hi = C.c_int64(), C.c_int64()
     lib().oq_paged_split_range(n_packed, n_res, S, s, C.byref(lo), C.byref(hi))
     return lo.value, hi.value
+
+
+# ---- outer-dimension (KIVI-style) grouping -------------------------------------------------
+
+def quantize_pack_outer(fmt: Format, src16, n_threads: int | None = None) -> np.ndarray:
+    """Blocks of src16[rows][T][d] (T a multiple of 128) with groups of 32 tokens per
+    channel; codes at the inner layout's positions, scale/zero as [4][d] per block."""
+    assert not fmt.hybrid, "outer grouping is asymmetric only"
+    src = np.ascontiguousarray(as_bits(src16))
+    rows, T, d = src.shape
+    nb = T // BLOCK
+    out = np.zeros((rows, nb * fmt.block_bytes), np.uint8)
+    rc = lib().oq_quantize_pack_outer(fmt.bits, d, _p(src), rows, T, T * d, d, _p(out),
+                                      out.shape[1], 0)
+    if rc != 0:
+        raise ValueError("bad arguments")
+    return out
+
+
+def attention_outer(fmt: Format, q16, Hkv: int, kp, vp, n_packed: int, kres16=None,
+                    vres16=None, n_res: int = 0, sm: float | None = None,
+                    n_threads: int | None = None):
+    """attention() over outer-grouped packed blocks."""
+    q, B, Hq, d, kp, vp, kres, vres, res_cap = _att_args(fmt, q16, Hkv, kp, vp, n_packed,
+                                                         kres16, vres16, n_res)
+    sm = float(np.float32(1.0 / np.sqrt(d))) if sm is None else sm
+    out = np.zeros((B, Hq, d), np.float64)
+    lib().oq_attention_outer(fmt.bits, d, _p(q), B, Hq, Hkv, _p(kp), _p(vp), kp.shape[1],
+                             n_packed, _p(kres), _p(vres), res_cap, n_res, sm, _p(out),
+                             n_threads or default_threads())
+    return out
+
+
+def split_attention_outer(fmt: Format, q16, Hkv: int, kp, vp, n_packed: int, kres16=None,
+                          vres16=None, n_res: int = 0, S: int = 1, sm: float | None = None,
+                          n_threads: int | None = None):
+    q, B, Hq, d, kp, vp, kres, vres, res_cap = _att_args(fmt, q16, Hkv, kp, vp, n_packed,
+                                                         kres16, vres16, n_res)
+    sm = float(np.float32(1.0 / np.sqrt(d))) if sm is None else sm
+    po = np.zeros((B, Hq, S, d), np.float64)
+    pl = np.zeros((B, Hq, S), np.float64)
+    lib().oq_split_attention_outer(fmt.bits, d, _p(q), B, Hq, Hkv, _p(kp), _p(vp), kp.shape[1],
+                                   n_packed, _p(kres), _p(vres), res_cap, n_res, sm, S, _p(po),
+                                   _p(pl), n_threads or default_threads())
+    return po, pl
