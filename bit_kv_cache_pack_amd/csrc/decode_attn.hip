@@ -40,6 +40,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace kvq {
 namespace {
 
@@ -94,6 +96,14 @@ struct WaveState {
 struct PVIn {
     uint32_t vc[8];
     uint32_t sd[8];
+};
+
+// The same for outer-grouped blocks: V codes as above, the {scale_v, zero_v} of channels
+// 8n .. 8n+7 for the tile's token group, and the tile's sum of p for head r.
+struct PVInO {
+    uint32_t vc[8];
+    uint32_t sz[8];
+    float P;
 };
 
 // Online-softmax step of stage A for one tile. lg[u]: logits (exp2 domain) of token 16u + n
@@ -243,6 +253,125 @@ __device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
     for (int c = 0; c < 8; ++c) st.dpv[c] *= alpha;
 }
 
+// ---------------------------------------------------------------------------------------
+// Outer-dimension groups (the KIVI-style comparison; a 32-token tile is exactly one token
+// group, and the tile's scale/zero region holds {scale, zero} per channel). With per-
+// channel scales the scale sits inside the Q K^T contraction, so it goes into the A
+// operand: A = q * scale_k per channel, split into an fp16 high part and the fp16 of the
+// remainder (two MFMAs, ~22 bits), B = the codes + 64 as before, and
+//     l_t = sum_c (q s)_c (code + 64) + sum_c q_c (zero_c - 64 s_c).
+// On the V side the scale varies along the output channels: each tile's P V (A = p, hi and
+// lo) is taken into fresh accumulators and added as scale_c * (P V)_c + zero'_c * sum_t p_t.
+// All of this is per tile, not per token.
+// ---------------------------------------------------------------------------------------
+template <int BITS>
+__device__ __forceinline__ void stage_a_outer(const uint8_t *slot, float *pw, const uint16_t *qw,
+                                              int NH, float sm_log2, const Magic &M, int lane,
+                                              int n, int r, WaveState &st, PVInO &pv,
+                                              float &alpha, bool &rescale)
+{
+    using G = TileGeom<BITS>;
+    const int hA = n >> 2, gA = n & 3;
+    const bool live = (gA == r) && (hA < NH);
+    KGroup<BITS> kc[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) kc[u].load(slot, 16 * u + n, r);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pv.vc[e] = v_octet<BITS>(slot + G::CB, 4 * e + r, n);
+    {
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(slot + G::VSZ + 32 * n);
+        const u32x4 b = *reinterpret_cast<const u32x4 *>(slot + G::VSZ + 32 * n + 16);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            pv.sz[k] = a[k];
+            pv.sz[4 + k] = b[k];
+        }
+    }
+    // octet o of the A operands (q * scale_k, hi and lo: channels 32 r + 8 o + i) is built
+    // just before its four MFMAs (two tokens halves x hi/lo); this lane's part of
+    // sum_c q_c zero'_c is summed on the way
+    float4_t acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    float zp = 0.0f;
+#pragma unroll
+    for (int o = 0; o < 4; ++o) {
+        const int c0 = 32 * r + 8 * o;
+        const u32x4 qv = *reinterpret_cast<const u32x4 *>(qw + hA * kHeadDim + c0);
+        const u32x4 s0 = *reinterpret_cast<const u32x4 *>(slot + G::KSZ + c0 * 4);
+        const u32x4 s1 = *reinterpret_cast<const u32x4 *>(slot + G::KSZ + c0 * 4 + 16);
+        u32x4 hi, lo;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const half2_t q2 = as_h2(qv[k]);
+            const uint32_t sa = k < 2 ? s0[2 * k] : s1[2 * k - 4];
+            const uint32_t sb = k < 2 ? s0[2 * k + 1] : s1[2 * k - 3];
+            const half2_t za = as_h2(sa), zb = as_h2(sb);      // {scale, zero} of the two channels
+            const float qa = (float)q2.x, qb = (float)q2.y;
+            const float pa = qa * (float)za.x, pb = qb * (float)zb.x;
+            const _Float16 ha = (_Float16)pa, hb = (_Float16)pb;
+            const _Float16 la = (_Float16)(pa - (float)ha), lb = (_Float16)(pb - (float)hb);
+            hi[k] = (uint32_t)__builtin_bit_cast(uint16_t, ha) | ((uint32_t)__builtin_bit_cast(uint16_t, hb) << 16);
+            lo[k] = (uint32_t)__builtin_bit_cast(uint16_t, la) | ((uint32_t)__builtin_bit_cast(uint16_t, lb) << 16);
+            zp = __builtin_fmaf(qa, __builtin_fmaf(-64.0f, (float)za.x, (float)za.y), zp);
+            zp = __builtin_fmaf(qb, __builtin_fmaf(-64.0f, (float)zb.x, (float)zb.y), zp);
+        }
+        const half8_t ah = live ? perm_octet_f16(hi) : half8_t{};
+        const half8_t al = live ? perm_octet_f16(lo) : half8_t{};
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const half8_t kb = kc[u].octet(o, M);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, kb, acc[u], 0, 0, 0);
+            acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, kb, acc[u], 0, 0, 0);
+        }
+    }
+    zp = live ? zp : 0.0f;
+    // Z'_r = sum over the four groups of head r: lanes 16 g + 4 r + g hold them
+    float zr = 0.0f;
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+        zr += __int_as_float(__builtin_amdgcn_ds_bpermute((16 * g + 4 * r + g) * 4, __float_as_int(zp)));
+    (void)lane;
+
+    float lg[2], zv[2][4];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        lg[u] = (((acc[u][0] + acc[u][1]) + (acc[u][2] + acc[u][3])) + zr) * sm_log2;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) zv[u][g] = 0.0f;
+    }
+    float p0, p1;
+    softmax_a(lg, zv, false, st, p0, p1, alpha, rescale);
+    pv.P = row_sum16(p0 + p1);
+    pw[r * kTile + slot_pos(n)] = p0;
+    pw[r * kTile + slot_pos(16 + n)] = p1;
+}
+
+template <int BITS>
+__device__ __forceinline__ void stage_b_outer(const float p8[8], const PVInO &pv, const Magic &M,
+                                              WaveState &st)
+{
+    half2_t vpair[4][8];
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(pv.vc[2 * mm], pv.vc[2 * mm + 1], M, vpair[mm]);
+    u32x4 ahi, alo;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        ahi[k] = pv_hi(p8[2 * k], 0x3C00u, p8[2 * k + 1], 0x3C00u);
+        alo[k] = pv_lo(p8[2 * k], 0x3C00u, p8[2 * k + 1], 0x3C00u, ahi[k]);
+    }
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const half8_t bv{vpair[0][c].x, vpair[0][c].y, vpair[1][c].x, vpair[1][c].y,
+                         vpair[2][c].x, vpair[2][c].y, vpair[3][c].x, vpair[3][c].y};
+        float4_t t = {0.f, 0.f, 0.f, 0.f};
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, ahi), bv, t, 0, 0, 0);
+        t = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, alo), bv, t, 0, 0, 0);
+        const half2_t sz = as_h2(pv.sz[c]);
+        const float sc = (float)sz.x;
+        const float zt = __builtin_fmaf(-64.0f, sc, (float)sz.y) * pv.P;   // zero' * sum p
+        st.dpv[c] += sc * t + zt;
+    }
+}
+
 // Merge the W waves' states of one workgroup through LDS (sm.mo, sm.ml) and write the
 // split's partials: part_o (normalised) and part_lse (natural log) of the chunk's NH heads,
 // query head hq0 + h. Every wave of the workgroup must call it.
@@ -304,7 +433,7 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
     }
 }
 
-template <int BITS, int NH, int RING, int W, bool PAGED>
+template <int BITS, int NH, int RING, int W, bool PAGED, bool OUTER = false>
 __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
                                                         const int32_t *__restrict__ tbl,
                                                         const int32_t *__restrict__ seq_state)
@@ -464,6 +593,22 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
     for (int g = 0; g < 4; ++g) st.zacc[g] = 0.0f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) st.dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
+    using PV = std::conditional_t<OUTER, PVInO, PVIn>;
+    const uint16_t *qw = &sm.q[wave][0][0];
+    // stage A / stage B of one packed tile, for the inner or the outer grouping
+    auto stage_a = [&](const uint8_t *slot, float *pw, PV &pv, float &alpha, bool &resc, int nv) {
+        if constexpr (OUTER) {
+            (void)nv;
+            stage_a_outer<BITS>(slot, pw, qw, NH, a.sm_log2, M, lane, n, r, st, pv, alpha, resc);
+        } else {
+            stage_a_packed<BITS, PAGED>(slot, pw, aq, qs, qinit, a.sm_log2, M, n, r, st, pv,
+                                        alpha, resc, nv);
+        }
+    };
+    auto stage_b = [&](const float p8[8], const PV &pv) {
+        if constexpr (OUTER) stage_b_outer<BITS>(p8, pv, M, st);
+        else stage_b_packed<BITS>(p8, pv, M, st);
+    };
 
     // ---- packed tiles through the ring, software-pipelined ----
     // Iteration k runs stage A (Q K^T, softmax, p) of tile k+1 next to stage B (P V) of
@@ -474,16 +619,15 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
     const int pstride = 4 * kTile;
     if (nt_w > 0) {
         wait_behind<BITS>(nt_w - 1 < RING - 1 ? nt_w - 1 : RING - 1);
-        PVIn cur;
+        PV cur;
         float alpha;
         bool resc;
         const int nv0 = tail_fix(ring, my_lo);
-        stage_a_packed<BITS, PAGED>(ring, pbuf, aq, qs, qinit, a.sm_log2, M, n, r, st, cur, alpha,
-                                    resc, nv0);
+        stage_a(ring, pbuf, cur, alpha, resc, nv0);
         wait_lgkm0();                                    // slot 0 read, p of tile 0 written
         if (RING < nt_w) issue(ring, my_lo + RING * kWaves);
         // one pipeline step: stage A of tile k+1 (into `nxt`) next to stage B of tile k
-        auto step = [&](int k, const PVIn &cur, PVIn &nxt) {
+        auto step = [&](int k, const PV &cur, PV &nxt) {
             // tile k+1 in LDS; the tiles up to k+RING may still be in flight
             wait_behind<BITS>(nt_w - 2 - k < RING - 1 ? nt_w - 2 - k : RING - 1);
             set_prio(nt_w - k);
@@ -491,22 +635,21 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
             const int nv = tail_fix(ring + s1 * G::BYTES, my_lo + (k + 1) * kWaves);
             float p8[8];
             load_p8(pbuf + (k & 1) * pstride, n, r, p8);
-            stage_a_packed<BITS, PAGED>(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, aq,
-                                        qs, qinit, a.sm_log2, M, n, r, st, nxt, alpha, resc, nv);
-            stage_b_packed<BITS>(p8, cur, M, st);
-            if (resc) rescale_pv(st, alpha);             // tile k's PV is in; tile k+1 moved m
+            stage_a(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, nxt, alpha, resc, nv);
+            stage_b(p8, cur);
+            if (resc) rescale_pv(st, alpha);      // tile k's PV is in; tile k+1 moved m
             wait_lgkm0();                                // slot k+1 read, p of tile k+1 written
             if (k + 1 + RING < nt_w) issue(ring + s1 * G::BYTES, my_lo + (k + 1 + RING) * kWaves);
         };
-        auto last = [&](int k, const PVIn &cur) {
+        auto last = [&](int k, const PV &cur) {
             float p8[8];
             load_p8(pbuf + (k & 1) * pstride, n, r, p8);
-            stage_b_packed<BITS>(p8, cur, M, st);
+            stage_b(p8, cur);
             wait_lgkm0();
         };
         // two steps per trip so that the stage-A output and stage-B input swap roles
         // instead of being copied
-        PVIn nxt;
+        PV nxt;
         int k = 0;
         for (; k + 2 < nt_w; k += 2) {
             step(k, cur, nxt);
@@ -799,6 +942,34 @@ hipError_t launch_paged_nh(const DecArgs &a, const int32_t *tbl, int bits, int n
     }
 }
 
+// outer-grouped blocks: the default ring depth only
+template <int BITS>
+hipError_t launch_outer_bits(const DecArgs &a, int nh, int64_t rows, int chunks,
+                             hipStream_t stream)
+{
+    constexpr int W = KVQ_WAVES;
+    const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
+    switch (nh) {
+    case 1: hipLaunchKernelGGL((decode_kernel<BITS, 1, KVQ_RING, W, false, true>), grid, dim3(64 * W), 0, stream, a, nullptr, nullptr); break;
+    case 2: hipLaunchKernelGGL((decode_kernel<BITS, 2, KVQ_RING, W, false, true>), grid, dim3(64 * W), 0, stream, a, nullptr, nullptr); break;
+    case 3: hipLaunchKernelGGL((decode_kernel<BITS, 3, KVQ_RING, W, false, true>), grid, dim3(64 * W), 0, stream, a, nullptr, nullptr); break;
+    case 4: hipLaunchKernelGGL((decode_kernel<BITS, 4, KVQ_RING, W, false, true>), grid, dim3(64 * W), 0, stream, a, nullptr, nullptr); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_outer_nh(const DecArgs &a, int bits, int nh, int64_t rows, int chunks,
+                           hipStream_t stream)
+{
+    switch (bits) {
+    case 2: return launch_outer_bits<2>(a, nh, rows, chunks, stream);
+    case 3: return launch_outer_bits<3>(a, nh, rows, chunks, stream);
+    case 4: return launch_outer_bits<4>(a, nh, rows, chunks, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 hipError_t launch_nh(const DecArgs &a, int bits, int nh, int64_t rows, int chunks, hipStream_t stream)
 {
     switch (bits) {
@@ -860,6 +1031,24 @@ hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream)
     if (tail > 0) {
         a.head_base = full * 4;
         e = launch_paged_nh(a, p.tbl, p.bits, tail, rows, 1, stream);
+    }
+    return e;
+}
+
+hipError_t launch_decode_outer(const DecodeParams &p, hipStream_t stream)
+{
+    DecArgs a = make_dec_args(p);
+    const int64_t rows = (int64_t)p.B * p.Hkv;
+    const int full = a.gq / 4, tail = a.gq % 4;
+    hipError_t e = hipSuccess;
+    if (full > 0) {
+        a.head_base = 0;
+        e = launch_outer_nh(a, p.bits, 4, rows, full, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) {
+        a.head_base = full * 4;
+        e = launch_outer_nh(a, p.bits, tail, rows, 1, stream);
     }
     return e;
 }

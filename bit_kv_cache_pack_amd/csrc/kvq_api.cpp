@@ -28,13 +28,18 @@ kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LA
 
 extern "C" {
 
-kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
-                             int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
-                             void *dst_packed, int64_t dst_row_stride_bytes,
-                             int32_t dst_first_block, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+kvq_status quantize_common(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                           int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                           void *dst_packed, int64_t dst_row_stride_bytes,
+                           int32_t dst_first_block, hipStream_t stream, bool outer)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
+    if (outer && fmt->hybrid) return KVQ_ERR_UNSUPPORTED;
     if (!src_fp16 || !dst_packed) return KVQ_ERR_NULL;
     if (n_rows < 1 || n_tokens < 128 || n_tokens % 128 != 0 || dst_first_block < 0)
         return KVQ_ERR_SHAPE;
@@ -46,11 +51,40 @@ kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_
     const int64_t nb = n_tokens / 128;
     if (dst_row_stride_bytes < ((int64_t)dst_first_block + nb) * bb) return KVQ_ERR_SHAPE;
     if (n_rows * nb > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (outer) {
+        return launched(kvq::launch_quantize_pack_outer(
+            fmt->bits, static_cast<const uint16_t *>(src_fp16), n_rows, n_tokens, src_row_stride,
+            src_tok_stride, static_cast<uint8_t *>(dst_packed), dst_row_stride_bytes,
+            dst_first_block, (int32_t)bb, (int32_t)kvq_sz_offset(fmt), stream));
+    }
     return launched(kvq::launch_quantize_pack(
         fmt->bits, fmt->hybrid, static_cast<const uint16_t *>(src_fp16), n_rows, n_tokens,
         src_row_stride, src_tok_stride, static_cast<uint8_t *>(dst_packed), dst_row_stride_bytes,
         dst_first_block, (int32_t)bb, (int32_t)kvq_sz_offset(fmt), (int32_t)kvq_flag_offset(fmt),
         stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize_pack(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                             int32_t n_tokens, int64_t src_row_stride, int64_t src_tok_stride,
+                             void *dst_packed, int64_t dst_row_stride_bytes,
+                             int32_t dst_first_block, hipStream_t stream)
+{
+    return quantize_common(fmt, src_fp16, n_rows, n_tokens, src_row_stride, src_tok_stride,
+                           dst_packed, dst_row_stride_bytes, dst_first_block, stream, false);
+}
+
+kvq_status kvq_quantize_pack_outer(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                                   int32_t n_tokens, int64_t src_row_stride,
+                                   int64_t src_tok_stride, void *dst_packed,
+                                   int64_t dst_row_stride_bytes, int32_t dst_first_block,
+                                   hipStream_t stream)
+{
+    return quantize_common(fmt, src_fp16, n_rows, n_tokens, src_row_stride, src_tok_stride,
+                           dst_packed, dst_row_stride_bytes, dst_first_block, stream, true);
 }
 
 }  // extern "C"
@@ -62,9 +96,11 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
                          int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
                          const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
                          int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
-                         float *part_lse, hipStream_t stream, bool valu,
+                         float *part_lse, hipStream_t stream, int kind,
                          const float *qnorm = nullptr)
 {
+    // kind: 0 the MFMA kernel, 1 the VALU comparison kernel, 2 outer-grouped blocks
+    if (kind == 2 && fmt && fmt->hybrid) return KVQ_ERR_UNSUPPORTED;
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
     if (!q_fp16 || !part_o || !part_lse) return KVQ_ERR_NULL;
@@ -109,7 +145,8 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
     p.qnorm = qnorm;
-    return launched(valu ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
+    if (kind == 2) return launched(kvq::launch_decode_outer(p, stream));
+    return launched(kind == 1 ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
 }
 
 }  // namespace
@@ -126,7 +163,7 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, false);
+                         num_splits, part_o, part_lse, stream, 0);
 }
 
 kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,
@@ -142,7 +179,20 @@ kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,
     if (!aligned64(key_norm)) return KVQ_ERR_ALIGN;
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, false, key_norm);
+                         num_splits, part_o, part_lse, stream, 0, key_norm);
+}
+
+kvq_status kvq_decode_attention_outer(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                      int32_t Hq, int32_t Hkv, const void *k_packed,
+                                      const void *v_packed, int64_t packed_row_stride_bytes,
+                                      int32_t n_packed_tokens, const void *k_res_fp16,
+                                      const void *v_res_fp16, int32_t res_capacity,
+                                      int32_t n_res, float sm_scale, int32_t num_splits,
+                                      float *part_o, float *part_lse, hipStream_t stream)
+{
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, part_o, part_lse, stream, 2);
 }
 
 kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -155,7 +205,7 @@ kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, 
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, true);
+                         num_splits, part_o, part_lse, stream, 1);
 }
 
 kvq_status kvq_decode_attention_fp16(const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv,

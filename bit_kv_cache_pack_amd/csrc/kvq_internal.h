@@ -36,6 +36,13 @@ struct DecodeParams {
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_outer(const DecodeParams &p, hipStream_t stream);
+
+hipError_t launch_quantize_pack_outer(int bits, const uint16_t *src, int64_t n_rows,
+                                      int32_t n_tokens, int64_t src_row_stride,
+                                      int64_t src_tok_stride, uint8_t *dst, int64_t dst_row_stride,
+                                      int32_t first_block, int32_t block_bytes, int32_t sz_off,
+                                      hipStream_t stream);
 hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream);
 
 hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,

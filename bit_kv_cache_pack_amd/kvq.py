@@ -25,7 +25,8 @@ _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
 EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_knorm",
             "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
             "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale", "kvq_pack_tokens_paged",
-            "kvq_append_evict", "kvq_decode_attention_paged")
+            "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
+            "kvq_decode_attention_outer")
 
 
 class KVQError(RuntimeError):
@@ -104,6 +105,8 @@ def lib():
         L.kvq_decode_attention.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp, vp, i32,
                                            i32, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_valu.argtypes = L.kvq_decode_attention.argtypes
+        L.kvq_decode_attention_outer.argtypes = L.kvq_decode_attention.argtypes
+        L.kvq_quantize_pack_outer.argtypes = L.kvq_quantize_pack.argtypes
         L.kvq_decode_attention_knorm.argtypes = [fp, vp, vp, i32, i32, i32, vp, vp, i64, i32,
                                                  vp, vp, i32, i32, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_fp16.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, f32, i32, vp,
@@ -168,6 +171,30 @@ def kvq_decode_attention(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packe
                                     float(sm_scale), num_splits, _ptr(part_o), _ptr(part_lse),
                                     _stream(stream, q_fp16))
     _check("kvq_decode_attention", st)
+
+
+def kvq_quantize_pack_outer(fmt: Format, src_fp16, n_rows: int, n_tokens: int,
+                            src_row_stride: int, src_tok_stride: int, dst_packed,
+                            dst_row_stride_bytes: int, dst_first_block: int, stream=None):
+    f = fmt.c()
+    st = lib().kvq_quantize_pack_outer(C.byref(f), _ptr(src_fp16), n_rows, n_tokens,
+                                       src_row_stride, src_tok_stride, _ptr(dst_packed),
+                                       dst_row_stride_bytes, dst_first_block,
+                                       _stream(stream, src_fp16, dst_packed))
+    _check("kvq_quantize_pack_outer", st)
+
+
+def kvq_decode_attention_outer(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
+                               v_packed, packed_row_stride_bytes: int, n_packed_tokens: int,
+                               k_res_fp16, v_res_fp16, res_capacity: int, n_res: int,
+                               sm_scale: float, num_splits: int, part_o, part_lse, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_outer(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_packed),
+                                          _ptr(v_packed), packed_row_stride_bytes,
+                                          n_packed_tokens, _ptr(k_res_fp16), _ptr(v_res_fp16),
+                                          res_capacity, n_res, float(sm_scale), num_splits,
+                                          _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
+    _check("kvq_decode_attention_outer", st)
 
 
 def kvq_decode_attention_knorm(fmt: Format, q_fp16, key_norm, B: int, Hq: int, Hkv: int,

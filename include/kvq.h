@@ -235,6 +235,44 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
                                 float *part_lse, hipStream_t stream);
 
 /*
+ * ---------------------------------------------------------------------------------
+ * Outer-dimension grouping (the comparison the InnerQ page draws: [InnerQ] sec. 1, the
+ * conventional KIVI-style grouping along the sequence; sec. 4.1, its timing)
+ * ---------------------------------------------------------------------------------
+ * A group is the 32 consecutive tokens 32*tg .. 32*tg+31 (tg = 0..3) of one channel of a
+ * 128-token block, for K and for V; the quantizer is the asymmetric one above (hybrid is
+ * not supported: KVQ_ERR_UNSUPPORTED). The block has the same size and regions as the
+ * inner format: the codes sit at the same positions (token-major, 32-channel LSB-first
+ * words), and the scale/zero region holds [4 token groups][head_dim channels]
+ * {fp16 scale, fp16 zero}. A value decodes as zero(tg, c) + code * scale(tg, c).
+ */
+
+/*
+ * kvq_quantize_pack_outer -- kvq_quantize_pack with outer-dimension groups. Arguments,
+ * validation and errors as kvq_quantize_pack; fmt->hybrid must be 0.
+ */
+kvq_status kvq_quantize_pack_outer(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,
+                                   int32_t n_tokens, int64_t src_row_stride,
+                                   int64_t src_tok_stride, void *dst_packed,
+                                   int64_t dst_row_stride_bytes, int32_t dst_first_block,
+                                   hipStream_t stream);
+
+/*
+ * kvq_decode_attention_outer -- kvq_decode_attention over outer-grouped blocks (same
+ * arguments, split rule, outputs and limits; fmt->hybrid must be 0). The per-channel
+ * scales sit inside the Q K^T contraction and along the P V output channels, so each
+ * 32-token tile takes q * scale_k as its MFMA operand and adds scale_v * (P V) + zero_v *
+ * sum(p) per channel; this is the cost of the outer grouping the comparison measures.
+ */
+kvq_status kvq_decode_attention_outer(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                      int32_t Hq, int32_t Hkv, const void *k_packed,
+                                      const void *v_packed, int64_t packed_row_stride_bytes,
+                                      int32_t n_packed_tokens, const void *k_res_fp16,
+                                      const void *v_res_fp16, int32_t res_capacity,
+                                      int32_t n_res, float sm_scale, int32_t num_splits,
+                                      float *part_o, float *part_lse, hipStream_t stream);
+
+/*
  * kvq_decode_attention_knorm -- kvq_decode_attention for a cache whose keys were
  * key-channel normalized ([InnerQ] sec. 2.4, see kvq_key_norm): every query channel is first
  * multiplied by the norm of its kv-head's row, q'[c] = fp16(q[c] * key_norm[b*Hkv + kvh][c])

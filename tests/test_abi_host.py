@@ -356,3 +356,21 @@ def test_suggest_splits_paged_bounds():
     for total, mx, hkv in [(32640, 32640, 8), (10 ** 7, 4096, 40), (100, 100, 1), (5000, 300, 2)]:
         s = K.suggest_splits_paged(total, mx, hkv)
         assert 1 <= s <= 256 and s <= max(1, mx // 256)
+
+
+def test_outer_calls_reject_hybrid_and_bad_shapes():
+    L = K.lib()
+    hyb = _fmt(hybrid=1)
+    assert L.kvq_quantize_pack_outer(C.byref(hyb), A, 2, 256, 256 * 128, 128, A, 2 * 10240, 0,
+                                     None) == K.KVQ_ERR_UNSUPPORTED
+    f = _fmt()
+    assert L.kvq_quantize_pack_outer(C.byref(f), None, 2, 256, 256 * 128, 128, A, 2 * 10240, 0,
+                                     None) == K.KVQ_ERR_NULL
+    assert L.kvq_quantize_pack_outer(C.byref(f), A, 2, 100, 256 * 128, 128, A, 2 * 10240, 0,
+                                     None) == K.KVQ_ERR_SHAPE
+    assert L.kvq_decode_attention_outer(C.byref(hyb), A, 1, 8, 2, A, A, 10240, 128, A, A, 128, 4,
+                                        0.088, 4, A, A, None) == K.KVQ_ERR_UNSUPPORTED
+    assert L.kvq_decode_attention_outer(C.byref(f), A, 1, 6, 4, A, A, 10240, 128, A, A, 128, 4,
+                                        0.088, 4, A, A, None) == K.KVQ_ERR_SHAPE
+    assert L.kvq_decode_attention_outer(C.byref(f), MIS, 1, 8, 2, A, A, 10240, 128, A, A, 128, 4,
+                                        0.088, 4, A, A, None) == K.KVQ_ERR_ALIGN
