@@ -10,8 +10,9 @@ To keep the 256 MB Infinity Cache (MALL) from serving the reads, the timed loop 
 over enough independent copies of the packed cache to exceed 512 MB. Also measured, and
 reported next to the step: the flush (kvq_quantize_pack of the 128-token window of every
 row), the one-token append, the key-channel normalization passes over the prefill keys and
-the decode step with normalized queries, the FP16 flash-decoding baseline, a plain device
-copy as a bandwidth reference, and the CPU oracle on a bounded sample of the same workload.
+the decode step with normalized queries, the FP16 flash-decoding baseline, the same step
+over outer-dimension (KIVI-style) groups, a serving-shaped paged batch, a plain device copy
+as a bandwidth reference, and the CPU oracle on a bounded sample of the same workload.
 
 Prints one JSON line.
 """
@@ -46,6 +47,7 @@ def parse():
     ap.add_argument("--no-fp16-baseline", action="store_true")
     ap.add_argument("--no-key-norm", action="store_true")
     ap.add_argument("--no-paged", action="store_true")
+    ap.add_argument("--no-outer", action="store_true")
     ap.add_argument("--paged-workload", default="paged_ragged_b16")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
@@ -319,6 +321,45 @@ def main():
                 "speedup_of_packed_decode_kernel": round(f16_dec_ms / dec_ms, 3)}
         del fcaches, kf0, vf0
 
+    # the outer-dimension (KIVI-style) grouping over the same tokens, same bytes per step:
+    # kvq_decode_attention_outer + kvq_combine, the comparison the InnerQ page draws
+    outer = None
+    if not args.no_outer and not wl.hybrid:
+        ocaches = []
+        for c in range(copies):
+            ko = torch.empty_like(kp0)
+            vo = torch.empty_like(vp0)
+            ocaches.append((ko, vo, caches[c][2], caches[c][3]))
+        ks_d = torch.from_numpy(np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128))).to(dev)
+        vs_d = torch.from_numpy(np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128))).to(dev)
+        for ko, vo, _, _ in ocaches:
+            K.kvq_quantize_pack_outer(fmt, ks_d, rows, wl.n_packed, wl.n_packed * 128, 128, ko,
+                                      nb * bb, 0)
+            K.kvq_quantize_pack_outer(fmt, vs_d, rows, wl.n_packed, wl.n_packed * 128, 128, vo,
+                                      nb * bb, 0)
+        del ks_d, vs_d
+
+        def decode_o(i, sp=sptr):
+            kp, vp, krd, vrd = ocaches[i % copies]
+            K.kvq_decode_attention_outer(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb,
+                                         wl.n_packed, krd, vrd, 128, wl.n_res, sm, S_, part_o,
+                                         part_lse, stream=sp)
+
+        def step_o(i, sp=sptr):
+            decode_o(i, sp)
+            K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+        o_step_ms = timed(step_o, args.steps, args.warmup)
+        o_dec_ms = timed(decode_o, args.steps, 5)
+        outer = {"us_per_step": round(o_step_ms * 1e3, 3),
+                 "decode_kernel_us": round(o_dec_ms * 1e3, 3),
+                 "GB_per_s_step": round(step_bytes / (o_step_ms * 1e-3) / 1e9, 1),
+                 "inner_speedup_step": round(o_step_ms / ms_per_step, 3),
+                 "inner_speedup_decode_kernel": round(o_dec_ms / dec_ms, 3)}
+        if fp16 is not None:
+            outer["speedup_over_fp16_step"] = round(fp16["us_per_step"] / (o_step_ms * 1e3), 3)
+        del ocaches
+
     # key-channel normalization: the once-per-prefill passes over the fp16 prefill keys
     # (kvq_key_norm: 2 B read per element; kvq_channel_scale: 2 B read + 2 B written), and
     # the decode step with q scaled inside the decode kernel (kvq_decode_attention_knorm)
@@ -442,6 +483,7 @@ def main():
                    "algorithmic_bytes_per_step": step_bytes},
         "fp16_baseline": fp16,
         "key_norm": knorm,
+        "outer_grouping": outer,
         "paged": paged,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
