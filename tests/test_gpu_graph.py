@@ -57,3 +57,86 @@ def test_graph_replays_match_eager():
         step(None)                      # eager work between replays
         torch.cuda.synchronize()
         assert torch.equal(out, ref_out)
+
+
+def test_paged_step_graph_replays_match_eager():
+    """One paged serving step (kvq_append_evict + kvq_decode_attention_paged + kvq_combine)
+    captured once and replayed for 40 steps, the new tokens and q copied in before each
+    replay: every step's output, and the pools, windows and sequence states at the end,
+    equal those of the same 40 steps run eagerly on a copy."""
+    from gpu_common import DEV, dev
+    import paged_common as P
+    rng = np.random.default_rng(5)
+    fmt = K.Format(4)
+    B, Hq, Hkv, cap, n_sink, S_, steps = 3, 8, 2, 16, 2, 3, 40
+    n_packed = [100, 0, 300]
+    n_res = [cap, 5, cap]
+    tbl, npool = P.make_table(rng, B, [P.blocks_for(n + steps + 1) for n in n_packed])
+    bb = fmt.block_bytes
+    kpool0 = dev(rng.integers(0, 256, (npool, Hkv, bb), dtype=np.uint8))
+    vpool0 = dev(rng.integers(0, 256, (npool, Hkv, bb), dtype=np.uint8))
+    # keep the packed bytes' scale/zero finite: pack real tokens into every used position
+    zero = torch.zeros(B, dtype=torch.int32, device=DEV)
+    cnt = dev(np.array(n_packed, np.int32))
+    src = dev(np.asarray(rng.standard_normal((B * Hkv, 300, 128)), np.float16))
+    dtbl = dev(tbl)
+    K.kvq_pack_tokens_paged(fmt, src, B, Hkv, 300 * 128, 128, cnt, zero, 300, kpool0, npool,
+                            Hkv * bb, bb, dtbl, tbl.shape[1])
+    K.kvq_pack_tokens_paged(fmt, src, B, Hkv, 300 * 128, 128, cnt, zero, 300, vpool0, npool,
+                            Hkv * bb, bb, dtbl, tbl.shape[1])
+    kres0 = dev(np.asarray(rng.standard_normal((B, Hkv, cap, 128)), np.float16))
+    vres0 = dev(np.asarray(rng.standard_normal((B, Hkv, cap, 128)), np.float16))
+    st0 = dev(np.array([[n_packed[b], n_res[b], n_sink, 0] for b in range(B)], np.int32))
+    new_k = dev(np.asarray(rng.standard_normal((steps, B, Hkv, 128)), np.float16))
+    new_v = dev(np.asarray(rng.standard_normal((steps, B, Hkv, 128)), np.float16))
+    qs = dev(np.asarray(rng.standard_normal((steps, B, Hq, 128)), np.float16))
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+
+    def make():
+        return [t.clone() for t in (kpool0, vpool0, kres0, vres0, st0)]
+
+    def step(bufs, kn, vn, q, po, pl, out, sp):
+        kp, vp, kr, vr, st = bufs
+        K.kvq_append_evict(fmt, kn, vn, kr, vr, cap, n_sink, kp, vp, npool, Hkv * bb, bb, dtbl,
+                           tbl.shape[1], st, B, Hkv, stream=sp)
+        K.kvq_decode_attention_paged(fmt, q, B, Hq, Hkv, kp, vp, npool, Hkv * bb, bb, dtbl,
+                                     tbl.shape[1], st, kr, vr, cap, sm, S_, po, pl, stream=sp)
+        K.kvq_combine(po, pl, B, Hq, 128, S_, out, K.KVQ_OUT_F32, stream=sp)
+
+    po = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((B, Hq, S_), dtype=torch.float32, device=DEV)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    print("[graph paged] eager", flush=True)
+    eager = make()
+    ref_out = []
+    for i in range(steps):
+        step(eager, new_k[i], new_v[i], qs[i], po, pl, out, None)
+        ref_out.append(out.clone())
+    torch.cuda.synchronize()
+
+    print("[graph paged] capture + replays", flush=True)
+    g_bufs = make()
+    kn_in, vn_in, q_in = new_k[0].clone(), new_v[0].clone(), qs[0].clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream(DEV)
+    g = torch.cuda.CUDAGraph()
+    # capture on a copy of the buffers, so that capturing does not advance the real ones
+    cap_bufs = make()
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g, stream=side):
+        step(cap_bufs, kn_in, vn_in, q_in, po, pl, out, torch.cuda.current_stream(DEV).cuda_stream)
+    torch.cuda.synchronize()
+    # the graph reads and writes cap_bufs: reset them to the initial state, then replay
+    for dst, srcb in zip(cap_bufs, g_bufs):
+        dst.copy_(srcb)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        kn_in.copy_(new_k[i])
+        vn_in.copy_(new_v[i])
+        q_in.copy_(qs[i])
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_out[i]), f"step {i}: output differs"
+    for a, b_, name in zip(cap_bufs, eager, ("K pool", "V pool", "K window", "V window", "state")):
+        assert torch.equal(a, b_), name
