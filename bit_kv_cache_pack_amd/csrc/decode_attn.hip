@@ -266,8 +266,8 @@ __device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
 // ---------------------------------------------------------------------------------------
 template <int BITS>
 __device__ __forceinline__ void stage_a_outer(const uint8_t *slot, float *pw, const uint16_t *qw,
-                                              int NH, float sm_log2, const Magic &M, int lane,
-                                              int n, int r, WaveState &st, PVInO &pv,
+                                              int NH, float sm_log2, const Magic &M, int n,
+                                              int r, WaveState &st, PVInO &pv,
                                               float &alpha, bool &rescale)
 {
     using G = TileGeom<BITS>;
@@ -329,7 +329,6 @@ __device__ __forceinline__ void stage_a_outer(const uint8_t *slot, float *pw, co
 #pragma unroll
     for (int g = 0; g < 4; ++g)
         zr += __int_as_float(__builtin_amdgcn_ds_bpermute((16 * g + 4 * r + g) * 4, __float_as_int(zp)));
-    (void)lane;
 
     float lg[2], zv[2][4];
 #pragma unroll
@@ -599,7 +598,7 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
     auto stage_a = [&](const uint8_t *slot, float *pw, PV &pv, float &alpha, bool &resc, int nv) {
         if constexpr (OUTER) {
             (void)nv;
-            stage_a_outer<BITS>(slot, pw, qw, NH, a.sm_log2, M, lane, n, r, st, pv, alpha, resc);
+            stage_a_outer<BITS>(slot, pw, qw, NH, a.sm_log2, M, n, r, st, pv, alpha, resc);
         } else {
             stage_a_packed<BITS, PAGED>(slot, pw, aq, qs, qinit, a.sm_log2, M, n, r, st, pv,
                                         alpha, resc, nv);
