@@ -370,8 +370,8 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
                                       const int32_t *block_table, int32_t max_blocks,
                                       const kvq_seq_state *state, const void *k_res_fp16,
                                       const void *v_res_fp16, int32_t res_capacity,
-                                      float sm_scale, int32_t num_splits, float *part_o,
-                                      float *part_lse, hipStream_t stream)
+                                      const float *key_norm, float sm_scale, int32_t num_splits,
+                                      float *part_o, float *part_lse, hipStream_t stream)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
@@ -386,13 +386,14 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
     if ((int64_t)B * Hq * fmt->head_dim * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
     if (!aligned64(q_fp16) || !aligned64(k_pool) || !aligned64(v_pool) || !aligned64(state) ||
         !aligned64(k_res_fp16) || !aligned64(v_res_fp16) || !aligned64(part_o) ||
-        !aligned64(part_lse))
+        !aligned64(part_lse) || (key_norm && !aligned64(key_norm)))
         return KVQ_ERR_ALIGN;
     kvq::PagedPool pp{};
     st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
                     max_blocks, pp);
     if (st != KVQ_OK) return st;
     kvq::DecodeParams p{};
+    p.qnorm = key_norm;
     p.q = static_cast<const uint16_t *>(q_fp16);
     p.B = B;
     p.Hq = Hq;

@@ -121,7 +121,8 @@ def lib():
         L.kvq_append_evict.argtypes = [fp, vp, vp, vp, vp, i32, i32, vp, vp, i64, i64, i64, vp,
                                        i32, vp, i32, i32, vp]
         L.kvq_decode_attention_paged.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64, i64,
-                                                 vp, i32, vp, vp, vp, i32, f32, i32, vp, vp, vp]
+                                                 vp, i32, vp, vp, vp, i32, vp, f32, i32, vp, vp,
+                                                 vp]
         for n in EXPORTED:
             getattr(L, n).restype = C.c_int
         _lib = L
@@ -294,14 +295,15 @@ def kvq_decode_attention_paged(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k
                                pool_blocks: int, block_stride_bytes: int,
                                head_stride_bytes: int, block_table, max_blocks: int, state,
                                k_res_fp16, v_res_fp16, res_capacity: int, sm_scale: float,
-                               num_splits: int, part_o, part_lse, stream=None):
+                               num_splits: int, part_o, part_lse, stream=None, key_norm=None):
     f = fmt.c()
     st = lib().kvq_decode_attention_paged(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_pool),
                                           _ptr(v_pool), pool_blocks, block_stride_bytes,
                                           head_stride_bytes, _ptr(block_table), max_blocks,
                                           _ptr(state), _ptr(k_res_fp16), _ptr(v_res_fp16),
-                                          res_capacity, float(sm_scale), num_splits,
-                                          _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
+                                          res_capacity, _ptr(key_norm), float(sm_scale),
+                                          num_splits, _ptr(part_o), _ptr(part_lse),
+                                          _stream(stream, q_fp16))
     _check("kvq_decode_attention_paged", st)
 
 

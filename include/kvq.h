@@ -460,6 +460,9 @@ kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void
  * the tiles, otherwise all S share them and split S-1 also takes the window; split s of
  * the Sp sharing splits gets tiles [s*NT/Sp, (s+1)*NT/Sp). Empty splits have lse = -inf
  * and o = 0; every sequence needs at least one token for kvq_combine to be defined.
+ *   key_norm        NULL, or the fp32 [B*Hkv][128] key-channel factors of a cache whose keys
+ *                   were normalized: q is then multiplied by them as in
+ *                   kvq_decode_attention_knorm (64-byte aligned)
  *   Other arguments, outputs and limits: as kvq_decode_attention.
  */
 kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -469,8 +472,8 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
                                       const int32_t *block_table, int32_t max_blocks,
                                       const kvq_seq_state *state, const void *k_res_fp16,
                                       const void *v_res_fp16, int32_t res_capacity,
-                                      float sm_scale, int32_t num_splits, float *part_o,
-                                      float *part_lse, hipStream_t stream);
+                                      const float *key_norm, float sm_scale, int32_t num_splits,
+                                      float *part_o, float *part_lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

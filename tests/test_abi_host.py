@@ -320,13 +320,14 @@ def test_append_evict_rejects(kw, status):
     assert _ae(**kw) == status
 
 
-def _dp(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, kr=A, vr=A, cap=128, sm=0.088,
-        S=4, po=A, pl=A, **kw):
+def _dp(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, kr=A, vr=A, cap=128, kn=None,
+        sm=0.088, S=4, po=A, pl=A, **kw):
     f = _fmt() if fmt is None else fmt
     p = _pool_kw(**kw)
     return K.lib().kvq_decode_attention_paged(C.byref(f), q, B, Hq, Hkv, kp, vp,
                                               p["pool_blocks"], p["bs"], p["hs"], p["tbl"],
-                                              p["maxb"], state, kr, vr, cap, sm, S, po, pl, None)
+                                              p["maxb"], state, kr, vr, cap, kn, sm, S, po, pl,
+                                              None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -344,6 +345,7 @@ def _dp(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, kr=A, vr=A, cap=12
     (dict(bs=3 * BB4 + 16), K.KVQ_ERR_ALIGN),
     (dict(pool_blocks=0), K.KVQ_ERR_SHAPE),
     (dict(fmt=_fmt(bits=6)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(kn=A + 8), K.KVQ_ERR_ALIGN),
 ])
 def test_decode_paged_rejects(kw, status):
     assert _dp(**kw) == status

@@ -350,3 +350,30 @@ def _paged_from_inputs(O, ofmt, wl, x):
     return dict(tbl=x.table, npool=x.n_pool_blocks, bs=wl.Hkv * ofmt.block_bytes,
                 hs=ofmt.block_bytes, kpool=kpool, vpool=vpool, kres=x.k_res, vres=x.v_res,
                 state=state, q=x.q, cap=x.k_res.shape[2])
+
+
+def test_paged_decode_with_key_norm_equals_scaled_q(oracle_mod):
+    """A paged cache of key-normalized keys: passing the factors to the paged decode gives
+    the partials of the paged decode on q multiplied by them with kvq_channel_scale."""
+    from gpu_common import DEV
+    O = oracle_mod
+    rng = np.random.default_rng(77)
+    fmt, ofmt = K.Format(4), O.Format(4)
+    B, Hq, Hkv, S_ = 3, 16, 4, 3
+    c = _paged_case(O, rng, fmt, ofmt, B, Hq, Hkv, [700, 33, 0], [10, 0, 64], 64)
+    norm = (2.0 ** rng.uniform(-3, 3, (B * Hkv, 128))).astype(np.float32)
+    nd, qd = _dev(norm), _dev(c["q"])
+    qs = torch.empty_like(qd)
+    K.kvq_channel_scale(qd, B * Hq, 1, 128, 128, 128, nd, Hq // Hkv, K.KVQ_SCALE_MULTIPLY, qs,
+                        128, 128)
+    args = (B, Hq, Hkv, _dev(c["kpool"]), _dev(c["vpool"]), c["npool"], c["bs"], c["hs"],
+            _dev(c["tbl"]), c["tbl"].shape[1], _dev(c["state"]), _dev(c["kres"]),
+            _dev(c["vres"]), c["cap"], SM, S_)
+    outs = []
+    for q, kn in ((qd, nd), (qs, None)):
+        po = torch.full((B, Hq, S_, 128), float("nan"), dtype=torch.float32, device=DEV)
+        pl = torch.full((B, Hq, S_), float("nan"), dtype=torch.float32, device=DEV)
+        K.kvq_decode_attention_paged(fmt, q, *args, po, pl, key_norm=kn)
+        outs.append((po, pl))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
