@@ -377,3 +377,120 @@ def test_paged_decode_with_key_norm_equals_scaled_q(oracle_mod):
         outs.append((po, pl))
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+
+
+def test_serving_run_with_key_normalization(oracle_mod):
+    """Everything together: per-sequence key-channel factors from the prompt keys, prompt
+    keys divided by them and packed into the pages, 60 steps whose new keys are divided
+    before they enter the window (kvq_channel_scale into a staging buffer, then
+    kvq_append_evict), and the paged decode with the factors -- all on the GPU -- against
+    the oracle doing the same steps."""
+    from gpu_common import DEV, assert_close
+    O = oracle_mod
+    rng = np.random.default_rng(123)
+    fmt, ofmt = K.Format(3), O.Format(3)
+    B, Hq, Hkv, cap, n_sink, steps, S_ = 2, 8, 2, 16, 2, 60, 3
+    prompt = [400, 150]
+    rows = B * Hkv
+    T = max(prompt)
+    ch_mult = np.ones(128, np.float32)
+    ch_mult[[5, 90]] = 9.0                                       # outlier key channels
+    toks_k = _f16(rng.standard_normal((rows, T, 128)) * ch_mult)
+    toks_v = _f16(rng.standard_normal((rows, T, 128)))
+    new_k = _f16(rng.standard_normal((steps, B, Hkv, 128)) * ch_mult)
+    new_v = _f16(rng.standard_normal((steps, B, Hkv, 128)))
+    q = _f16(rng.standard_normal((B, Hq, 128)))
+    tbl, npool = P.make_table(rng, B, [P.blocks_for(p + steps) for p in prompt])
+    shape, bs, hs = _layout("block_major", npool, Hkv, fmt.block_bytes)
+    # prompt split: sinks + recent in the window, the middle packed (per sequence)
+    count = np.zeros(B, np.int32)
+    state = np.zeros((B, 4), np.int32)
+    mid_idx = []
+    for b, n in enumerate(prompt):
+        m = n - cap
+        count[b] = m
+        state[b] = [m, cap, n_sink, 0]
+        mid_idx.append(np.arange(n_sink, n_sink + m))
+    # ---- oracle
+    norm = np.zeros((rows, 128), np.float32)
+    for b, n in enumerate(prompt):                    # factors over each sequence's prompt
+        norm[b * Hkv:(b + 1) * Hkv] = O.key_norm(toks_k[b * Hkv:(b + 1) * Hkv, :n])
+    kn_all = O.channel_scale(toks_k, norm).view(np.float16)
+    mid_k = np.zeros((rows, T, 128), np.float16)
+    mid_v = np.zeros_like(mid_k)
+    kres = np.zeros((B, Hkv, cap, 128), np.float16)
+    vres = np.zeros_like(kres)
+    for b, n in enumerate(prompt):
+        r = slice(b * Hkv, (b + 1) * Hkv)
+        mid_k[r, :count[b]] = kn_all[r][:, mid_idx[b]]
+        mid_v[r, :count[b]] = toks_v[r][:, mid_idx[b]]
+        kres[b, :, :n_sink] = kn_all[r, :n_sink]
+        vres[b, :, :n_sink] = toks_v[r, :n_sink]
+        kres[b, :, n_sink:] = kn_all[r, n - (cap - n_sink):n]
+        vres[b, :, n_sink:] = toks_v[r, n - (cap - n_sink):n]
+    okp = np.full(shape, 0xFF, np.uint8)
+    ovp = np.full(shape, 0xFF, np.uint8)
+    zero = np.zeros(B, np.int32)
+    O.pack_tokens_paged(ofmt, mid_k, B, Hkv, count, zero, okp, tbl)
+    O.pack_tokens_paged(ofmt, mid_v, B, Hkv, count, zero, ovp, tbl)
+    okr, ovr, ost = kres.copy(), vres.copy(), state.copy()
+    for i in range(steps):
+        kn = O.channel_scale(new_k[i].reshape(rows, 1, 128), norm).view(np.float16).reshape(B, Hkv, 128)
+        O.append_evict(ofmt, kn, new_v[i], okr, ovr, n_sink, okp, ovp, tbl, ost)
+    qn = O.channel_scale(q.reshape(B * Hq, 1, 128), norm, rows_per_norm=Hq // Hkv,
+                         multiply=True).view(np.float16).reshape(B, Hq, 128)
+    ref = O.attention_paged(ofmt, qn, Hkv, okp, ovp, tbl, ost, okr, ovr, sm=SM)
+
+    # ---- GPU
+    print("[serving+knorm] prefill", flush=True)
+    dk_all = _dev(toks_k)
+    dnorm = torch.empty((rows, 128), dtype=torch.float32, device=DEV)
+    for b, n in enumerate(prompt):
+        K.kvq_key_norm(dk_all[b * Hkv:(b + 1) * Hkv], Hkv, n, T * 128, 128, 128,
+                       dnorm[b * Hkv:(b + 1) * Hkv])
+    K.kvq_channel_scale(dk_all, rows, T, T * 128, 128, 128, dnorm, 1, K.KVQ_SCALE_DIVIDE, dk_all,
+                        T * 128, 128)
+    torch.cuda.synchronize()
+    assert np.array_equal(dnorm.cpu().numpy().view(np.uint32), norm.view(np.uint32))
+    assert np.array_equal(dk_all.cpu().numpy().view(np.uint16), kn_all.view(np.uint16))
+    # the same split of the prompt, gathered on the GPU from the normalized keys
+    dmid_k = torch.zeros((rows, T, 128), dtype=torch.float16, device=DEV)
+    dmid_v = torch.zeros_like(dmid_k)
+    dv_all = _dev(toks_v)
+    dkres = torch.zeros((B, Hkv, cap, 128), dtype=torch.float16, device=DEV)
+    dvres = torch.zeros_like(dkres)
+    for b, n in enumerate(prompt):
+        r = slice(b * Hkv, (b + 1) * Hkv)
+        idx = torch.from_numpy(mid_idx[b]).to(DEV)
+        dmid_k[r, :count[b]] = dk_all[r][:, idx]
+        dmid_v[r, :count[b]] = dv_all[r][:, idx]
+        dkres[b, :, :n_sink] = dk_all[r, :n_sink]
+        dvres[b, :, :n_sink] = dv_all[r, :n_sink]
+        dkres[b, :, n_sink:] = dk_all[r, n - (cap - n_sink):n]
+        dvres[b, :, n_sink:] = dv_all[r, n - (cap - n_sink):n]
+    dk, dv = _dev(np.full(shape, 0xFF, np.uint8)), _dev(np.full(shape, 0xFF, np.uint8))
+    dtbl, dcount, dzero = _dev(tbl), _dev(count), _dev(zero)
+    K.kvq_pack_tokens_paged(fmt, dmid_k, B, Hkv, T * 128, 128, dcount, dzero, T, dk, npool, bs, hs,
+                            dtbl, tbl.shape[1])
+    K.kvq_pack_tokens_paged(fmt, dmid_v, B, Hkv, T * 128, 128, dcount, dzero, T, dv, npool, bs, hs,
+                            dtbl, tbl.shape[1])
+    dkr, dvr, dst = dkres, dvres, _dev(state)
+    dnk, dnv = _dev(new_k), _dev(new_v)
+    stage = torch.empty((B, Hkv, 128), dtype=torch.float16, device=DEV)
+    print("[serving+knorm] steps", flush=True)
+    for i in range(steps):
+        K.kvq_channel_scale(dnk[i], rows, 1, 128, 128, 128, dnorm, 1, K.KVQ_SCALE_DIVIDE, stage,
+                            128, 128)
+        K.kvq_append_evict(fmt, stage, dnv[i], dkr, dvr, cap, n_sink, dk, dv, npool, bs, hs, dtbl,
+                           tbl.shape[1], dst, B, Hkv)
+    po = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((B, Hq, S_), dtype=torch.float32, device=DEV)
+    K.kvq_decode_attention_paged(fmt, _dev(q), B, Hq, Hkv, dk, dv, npool, bs, hs, dtbl,
+                                 tbl.shape[1], dst, dkr, dvr, cap, SM, S_, po, pl, key_norm=dnorm)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    K.kvq_combine(po, pl, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
+    torch.cuda.synchronize()
+    assert np.array_equal(dst.cpu().numpy(), ost)
+    assert np.array_equal(dk.cpu().numpy(), okp) and np.array_equal(dv.cpu().numpy(), ovp)
+    assert np.array_equal(dkr.cpu().numpy().view(np.uint16), okr.view(np.uint16))
+    assert_close(out.cpu().numpy(), ref, "serving run with key normalization")
