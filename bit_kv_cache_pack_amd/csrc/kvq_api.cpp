@@ -26,10 +26,6 @@ kvq_status launched(hipError_t e) { return e == hipSuccess ? KVQ_OK : KVQ_ERR_LA
 
 }  // namespace
 
-extern "C" {
-
-}  // extern "C"
-
 namespace {
 
 kvq_status quantize_common(const kvq_format *fmt, const void *src_fp16, int64_t n_rows,

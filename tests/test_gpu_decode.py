@@ -96,6 +96,8 @@ CASES = [
     (4, False, 1, 8, 2, 0, 128, 1),        # all tokens in the fp16 window
     (4, False, 1, 8, 2, 0, 5, 3),          # tiny residual only, empty packed splits
     (4, False, 1, 8, 2, 128, 0, 1),        # one block, one split
+    (4, False, 1, 8, 2, 32768, 128, 1024), # the split limit: one 32-token tile per split
+    (3, True, 1, 8, 2, 1024, 9, 1024),     # the split limit, almost every split empty
 ]
 
 

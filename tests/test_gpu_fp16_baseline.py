@@ -45,6 +45,7 @@ def _run(oracle_mod, B, Hq, Hkv, L, S_, stride=None, seed=0, scale=1.0):
     (1, 20, 2, 300, 3),     # gq 10 (chunks + tail)
     (1, 32, 2, 2048, 16),   # gq 16
     (3, 32, 8, 4096, 8),
+    (1, 8, 2, 32768, 1024),  # the split limit: one 32-token tile per split
 ])
 def test_fp16_baseline_small(oracle_mod, B, Hq, Hkv, L, S_):
     _run(oracle_mod, B, Hq, Hkv, L, S_, seed=B + Hq + L + S_)

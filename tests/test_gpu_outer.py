@@ -73,6 +73,7 @@ CASES = [
     (2, 3, 4, 4, 256, 5, 2),
     (4, 1, 12, 2, 384, 1, 4),        # 6 heads per kv head: chunks of 4 and 2
     (2, 1, 8, 1, 0, 70, 1),          # window only
+    (4, 1, 8, 2, 16384, 128, 1024),  # the split limit
 ]
 
 

@@ -178,6 +178,7 @@ DECODE_CASES = [
     (2, False, 5, 16, 16, [1, 2, 127, 128, 129], [1, 0, 0, 7, 2], 8, 1, "block_major"),
     (2, True, 2, 12, 1, [2000, 95], [0, 1], 4, 7, "head_major"),
     (4, False, 2, 20, 2, [640, 333], [16, 16], 16, 4, "block_major"),   # 10 heads: chunks 4+4+2
+    (4, False, 2, 8, 2, [32768, 700], [128, 3], 128, 1024, "head_major"),  # the split limit
 ]
 
 
