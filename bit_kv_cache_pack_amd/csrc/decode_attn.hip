@@ -17,21 +17,24 @@
 //    and for tile k+2 once tile k is consumed (2 slots) or has arrived (3 slots), so ~10 KB
 //    per wave is in flight without holding it in VGPRs; the wave waits on vmcnt for
 //    exactly the tile it is about to use.
-//  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the integer codes plus 64 (exact in fp16,
-//    made with the fp16 magic-number trick) and rows i = 4*head + group of A holding the
-//    query restricted to one 32-channel group; the accumulator starts at -64 * sum(q over
-//    the group), which removes the offset. Lane (token n, r) loads group r of token n
-//    (one 16/12/8-byte load), and MFMA o consumes that group's channel octet o, so the
-//    result row 4h+g is head h's dot product with group g's codes. Every lane then holds
-//    the four group dots of one (token, head) and applies its token's scale/zero:
+//  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the integer codes as fp16 subnormals
+//    (a code masked into mantissa bits k.. of a zero-exponent half is exactly
+//    code * 2^(k-24); one AND per pair of codes) and rows i = 4*head + group of A holding
+//    the query restricted to one 32-channel group, each channel divided by the power of
+//    two its code slot carries. Lane (token n, r) loads group r of token n (one
+//    16/12/8-byte load), and MFMA o consumes that group's channel octet o, so the result
+//    row 4h+g is 2^-24 times head h's dot product with group g's codes. Every lane then
+//    holds the four group dots of one (token, head) and applies its token's scale/zero:
 //        l = sum_g scale_g * dot_g + zero_g * sum(q over g)
 //    with no cross-lane reduction.
 //  * P V uses the same MFMA with rows i = 4*head + group holding p * scale_v (split into
 //    an fp16 high part and an fp16 remainder, two MFMAs, so the weights keep ~22 bits)
-//    and B = the V codes (plus 64) of 8 tokens x 1 channel per lane, built from two
-//    tokens' code words at a time. Only rows whose group matches the column's group are
-//    used; the zero-point term sum_t p_t zero'_v (zero' = zero - 64 * scale) is
+//    and B = the V codes (again subnormals) of 8 tokens x 1 channel per lane, built from
+//    two tokens' code words at a time; each accumulator column is one channel, so its
+//    power-of-two weight is divided out once after the last tile. Only rows whose group
+//    matches the column's group are used; the zero-point term sum_t p_t zero_v is
 //    accumulated on the VALU.
+//    (The outer-grouped variant keeps codes + 64 from the fp16 magic-number trick.)
 //  * row (16-lane) max / sum reductions use DPP; p passes through a 512 B per-wave LDS
 //    slice to reach the PV operand layout, and the V scales are read straight from the
 //    staged tile.
@@ -86,7 +89,7 @@ __device__ __forceinline__ float sel4(float4_t v, int k)
 // Online-softmax state of one wave: lane (n, r) tracks head r.
 struct WaveState {
     float m, l;
-    float zacc[4];     // sum_t p_t * zero'_v(t, g) for head r, group g (lane partial)
+    float zacc[4];     // sum_t p_t * zero_v(t, g) for head r, group g (lane partial)
     float4_t dpv[8];   // PV accumulators: rows 4h+g, column n <-> channel 8n + c
 };
 
@@ -172,22 +175,32 @@ __device__ __forceinline__ void pv_mfma(const float p8[8], const uint32_t sd[8],
 }
 
 template <int BITS>
-__device__ __forceinline__ void stage_b_packed(const float p8[8], const PVIn &pv, const Magic &M,
-                                               WaveState &st)
+__device__ __forceinline__ void raw_pair(uint32_t a, uint32_t b, half2_t out[8])
+{
+    if (BITS == 4) raw_pair4(a, b, out);
+    else if (BITS == 2) raw_pair2(a, b, out);
+    else raw_pair3(a, b, out);
+}
+
+// Stage B of a packed tile: the V codes enter as subnormals, so dpv[c] collects
+// 2^(raw_value_shift(c) - 24) * sum_t p_t scale_t code_t (undone after the last tile).
+template <int BITS>
+__device__ __forceinline__ void stage_b_packed(const float p8[8], const PVIn &pv, WaveState &st)
 {
     half2_t vpair[4][8];
 #pragma unroll
-    for (int mm = 0; mm < 4; ++mm) pair_tokens<BITS>(pv.vc[2 * mm], pv.vc[2 * mm + 1], M, vpair[mm]);
+    for (int mm = 0; mm < 4; ++mm) raw_pair<BITS>(pv.vc[2 * mm], pv.vc[2 * mm + 1], vpair[mm]);
     pv_mfma(p8, pv.sd, vpair, st);
 }
 
 // Stage A of a packed tile in LDS slot `slot`: Q K^T, softmax step, p -> pw (this wave's
 // p buffer), and what stage B will need, copied out of the slot into registers. With MASK,
-// tokens nvalid .. 31 of the tile are not attended (their logits are -inf).
+// tokens nvalid .. 31 of the tile are not attended (their logits are -inf). aq: the query
+// octets divided by the key slots' weights, so the MFMA gives 2^-24 * sum_c q_c code_c;
+// qs24: 2^-24 * sum(q over group g); sm24: 2^24 * sm_scale * log2(e).
 template <int BITS, bool MASK = false>
 __device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, const half8_t aq[4],
-                                               const float qs[4], const float4_t qinit,
-                                               float sm_log2, const Magic &M, int n, int r,
+                                               const float qs24[4], float sm24, int n, int r,
                                                WaveState &st, PVIn &pv, float &alpha,
                                                bool &rescale, int nvalid = kTile)
 {
@@ -210,28 +223,23 @@ __device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, c
     float lg[2], zv[2][4];
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-        // the K operand carries codes + 64; starting from -64 * sum(q over g) removes it
-        float4_t acc = qinit;
+        float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int o = 0; o < 4; ++o)
-            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[o], kc[u].octet(o, M), acc, 0, 0, 0);
-        // l = sum_g scale_g * dot_g + zero_g * sum(q over g), as two chains of two groups
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq[o], kc[u].raw(o), acc, 0, 0, 0);
+        // 2^-24 l = sum_g scale_g * dot_g + zero_g * sum(q over g), two chains of two groups
         float s01 = 0.0f, s23 = 0.0f;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
             const half2_t a = as_h2(ksz[u][g]), c = as_h2(ksz[u][g + 2]);
             s01 = __builtin_fmaf((float)a.x, acc[g], s01);
-            s01 = __builtin_fmaf((float)a.y, qs[g], s01);
+            s01 = __builtin_fmaf((float)a.y, qs24[g], s01);
             s23 = __builtin_fmaf((float)c.x, acc[g + 2], s23);
-            s23 = __builtin_fmaf((float)c.y, qs[g + 2], s23);
+            s23 = __builtin_fmaf((float)c.y, qs24[g + 2], s23);
         }
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-            const half2_t szv = as_h2(vsz[u][g]);
-            // the V operand carries codes + 64: zero' = zero - 64 * scale
-            zv[u][g] = __builtin_fmaf(-64.0f, (float)szv.x, (float)szv.y);
-        }
-        lg[u] = (s01 + s23) * sm_log2;
+        for (int g = 0; g < 4; ++g) zv[u][g] = (float)as_h2(vsz[u][g]).y;
+        lg[u] = (s01 + s23) * sm24;
         if (MASK && 16 * u + n >= nvalid) lg[u] = -INFINITY;
     }
     // any V scale of the tile at or above 2^(15 - kSlack)? (fp16 compare on the low halves)
@@ -553,16 +561,26 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
     }
 
     // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
+    // The query octets in the key operand's slot order; for the packed tiles slot pair p is
+    // divided by the weight 2^raw_key_shift(p) its subnormal codes carry (exact in fp16 but
+    // for values that become subnormal; the fp16 window rebuilds them undivided).
     half8_t aq[4];
-    {
+    auto build_aq = [&](bool weighted) {
         const int hA = n >> 2, gA = n & 3;
         const bool live = (gA == r) && (hA < NH);
 #pragma unroll
         for (int o = 0; o < 4; ++o) {
             const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hA][32 * r + 8 * o]);
-            aq[o] = live ? perm_octet_f16(w) : half8_t{};
+            half8_t h = live ? perm_octet_f16(w) : half8_t{};
+            if (weighted) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    h[i] = (_Float16)((float)h[i] * (1.0f / (float)(1 << raw_key_shift<BITS>(i >> 1))));
+            }
+            aq[o] = h;
         }
-    }
+    };
+    build_aq(!OUTER);
     float qs[4];
     {
         // lane (hh, gg, qq) sums 8 channels; the quad sum is Qs[hh][gg]; lane (n, r) then
@@ -582,7 +600,8 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
         for (int g = 0; g < 4; ++g)
             qs[g] = __int_as_float(__builtin_amdgcn_ds_bpermute((16 * r + 4 * g) * 4, __float_as_int(s)));
     }
-    const float4_t qinit = {-64.0f * qs[0], -64.0f * qs[1], -64.0f * qs[2], -64.0f * qs[3]};
+    const float qs24[4] = {qs[0] * 0x1p-24f, qs[1] * 0x1p-24f, qs[2] * 0x1p-24f, qs[3] * 0x1p-24f};
+    const float sm24 = a.sm_log2 * 0x1p24f;
 
     const Magic M;
     WaveState st;
@@ -600,13 +619,12 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
             (void)nv;
             stage_a_outer<BITS>(slot, pw, qw, NH, a.sm_log2, M, n, r, st, pv, alpha, resc);
         } else {
-            stage_a_packed<BITS, PAGED>(slot, pw, aq, qs, qinit, a.sm_log2, M, n, r, st, pv,
-                                        alpha, resc, nv);
+            stage_a_packed<BITS, PAGED>(slot, pw, aq, qs24, sm24, n, r, st, pv, alpha, resc, nv);
         }
     };
     auto stage_b = [&](const float p8[8], const PV &pv) {
         if constexpr (OUTER) stage_b_outer<BITS>(p8, pv, M, st);
-        else stage_b_packed<BITS>(p8, pv, M, st);
+        else stage_b_packed<BITS>(p8, pv, st);
     };
 
     // ---- packed tiles through the ring, software-pipelined ----
@@ -660,10 +678,18 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
         } else {
             last(k, cur);
         }
+        if constexpr (!OUTER) {
+            // the V codes entered as subnormals: column c of every octet weighed
+            // 2^(raw_value_shift(c) - 24); back to value units (exact)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                st.dpv[c] *= (float)(1 << (24 - raw_value_shift<BITS>(c)));
+        }
     }
 
     // ---- residual / sink tokens (fp16), in 32-token tiles ----
     if (with_res) {
+        if constexpr (!OUTER) build_aq(false);
         const uint16_t *kr = a.kres + row * a.res_cap * kHeadDim;
         const uint16_t *vr = a.vres + row * a.res_cap * kHeadDim;
         const int n_rt = (n_res_b + kTile - 1) / kTile;

@@ -167,6 +167,7 @@ struct KGroup<4> {
         w = *reinterpret_cast<const u32x4 *>(slot + t * 64 + r * 16);
     }
     __device__ __forceinline__ half8_t octet(int o, const Magic &M) const { return unpack_octet4(w[o], M); }
+    __device__ __forceinline__ half8_t raw(int o) const { return raw_octet4(w[o]); }
 };
 template <>
 struct KGroup<2> {
@@ -178,6 +179,10 @@ struct KGroup<2> {
     __device__ __forceinline__ half8_t octet(int o, const Magic &M) const
     {
         return unpack_octet2((o & 1) ? (w[o >> 1] >> 16) : w[o >> 1], M);
+    }
+    __device__ __forceinline__ half8_t raw(int o) const
+    {
+        return raw_octet2((o & 1) ? (w[o >> 1] >> 16) : w[o >> 1]);
     }
 };
 template <>
@@ -195,6 +200,12 @@ struct KGroup<3> {
         const uint32_t x = o == 0 ? w0 : o == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
                                      : o == 2 ? __builtin_amdgcn_alignbit(w2, w1, 16) : (w2 >> 8);
         return unpack_octet3(x, M);
+    }
+    __device__ __forceinline__ half8_t raw(int o) const
+    {
+        const uint32_t x = o == 0 ? w0 : o == 1 ? __builtin_amdgcn_alignbit(w1, w0, 24)
+                                     : o == 2 ? __builtin_amdgcn_alignbit(w2, w1, 16) : (w2 >> 8);
+        return raw_octet3(x);
     }
 };
 

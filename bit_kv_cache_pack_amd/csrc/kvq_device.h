@@ -171,4 +171,101 @@ __device__ __forceinline__ void pair_tokens3(uint32_t a, uint32_t b, const Magic
     out[7] = as_h2(mpair(hi >> 5, m, M.b6));
 }
 
+// ---- codes as fp16 subnormals ---------------------------------------------------------
+// With a zero exponent field, fp16 mantissa bits [k, k + b) holding a code c give the
+// subnormal value c * 2^(k - 24), exactly, and the gfx950 matrix cores multiply subnormal
+// fp16 operands at their value. So a pair of codes (one per 16-bit half) becomes an MFMA
+// operand with a single mask: no offset to add and none to remove, as long as the code
+// sits inside bits 0..9. Each slot pair then carries a power-of-two weight 2^k (in units
+// of 2^-24) that the other operand or the accumulator divides out exactly.
+//
+// Key operand: eight codes of one channel octet, in the slot order (0,4,1,5,2,6,3,7) of the
+// query operand; slot pair p holds channels p and p + 4 with weight 2^raw_key_shift<BITS>(p).
+template <int BITS>
+__device__ __forceinline__ constexpr int raw_key_shift(int p)
+{
+    return BITS == 4 ? (p & 1) * 4 : BITS == 2 ? 2 * p : (p == 0 ? 0 : p == 1 ? 3 : 6);
+}
+//  4-bit: the octet is a 32-bit word, code i at bits 4i
+__device__ __forceinline__ half8_t raw_octet4(uint32_t w)
+{
+    const uint32_t t = w >> 8;
+    const half2_t p0 = as_h2(w & 0x000F000Fu);   // c0,c4  x1
+    const half2_t p1 = as_h2(w & 0x00F000F0u);   // c1,c5  x16
+    const half2_t p2 = as_h2(t & 0x000F000Fu);   // c2,c6  x1
+    const half2_t p3 = as_h2(t & 0x00F000F0u);   // c3,c7  x16
+    return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+//  2-bit: the octet is 16 bits (low half of y), code i at bits 2i
+__device__ __forceinline__ half8_t raw_octet2(uint32_t y)
+{
+    const uint32_t w = perm_b32(0u, y, 0x0c010c00u);   // byte 0 -> low half, byte 1 -> high
+    const half2_t p0 = as_h2(w & 0x00030003u);   // c0,c4  x1
+    const half2_t p1 = as_h2(w & 0x000C000Cu);   // c1,c5  x4
+    const half2_t p2 = as_h2(w & 0x00300030u);   // c2,c6  x16
+    const half2_t p3 = as_h2(w & 0x00C000C0u);   // c3,c7  x64
+    return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+//  3-bit: the octet is 24 bits (low bits of x), code i at bits 3i
+__device__ __forceinline__ half8_t raw_octet3(uint32_t x)
+{
+    const uint32_t w = pack_lo16(x, x >> 12);            // c0..c3 low half, c4..c7 high half
+    const half2_t p0 = as_h2(w & 0x00070007u);           // c0,c4  x1
+    const half2_t p1 = as_h2(w & 0x00380038u);           // c1,c5  x8
+    const half2_t p2 = as_h2(w & 0x01C001C0u);           // c2,c6  x64
+    const half2_t p3 = as_h2((w >> 3) & 0x01C001C0u);    // c3,c7  x64 (bits 9-11 -> 6-8)
+    return half8_t{p0.x, p0.y, p1.x, p1.y, p2.x, p2.y, p3.x, p3.y};
+}
+
+// Value operand: for each channel c of the octet a half2 {code(a, c), code(b, c)} of two
+// tokens' octets, with weight 2^raw_value_shift<BITS>(c).
+template <int BITS>
+__device__ __forceinline__ constexpr int raw_value_shift(int c)
+{
+    return BITS == 4 ? (c & 1) * 4
+         : BITS == 2 ? (c < 5 ? 2 * c : 2 * c - 6)
+                     : ((c & 3) == 0 ? 0 : (c & 3) == 1 ? 3 : 6);
+}
+__device__ __forceinline__ void raw_pair4(uint32_t a, uint32_t b, half2_t out[8])
+{
+    const uint32_t lo = pack_lo16(a, b);   // channels 0..3 of both tokens
+    const uint32_t hi = pack_hi16(a, b);   // channels 4..7
+    const uint32_t lt = lo >> 8, ht = hi >> 8;
+    out[0] = as_h2(lo & 0x000F000Fu);
+    out[1] = as_h2(lo & 0x00F000F0u);
+    out[2] = as_h2(lt & 0x000F000Fu);
+    out[3] = as_h2(lt & 0x00F000F0u);
+    out[4] = as_h2(hi & 0x000F000Fu);
+    out[5] = as_h2(hi & 0x00F000F0u);
+    out[6] = as_h2(ht & 0x000F000Fu);
+    out[7] = as_h2(ht & 0x00F000F0u);
+}
+__device__ __forceinline__ void raw_pair2(uint32_t a, uint32_t b, half2_t out[8])
+{
+    const uint32_t u = pack_lo16(a, b);    // 16-bit octets side by side
+    const uint32_t t = u >> 6;             // channels 5..7 (bits 10-15) -> bits 4-9
+    out[0] = as_h2(u & 0x00030003u);
+    out[1] = as_h2(u & 0x000C000Cu);
+    out[2] = as_h2(u & 0x00300030u);
+    out[3] = as_h2(u & 0x00C000C0u);
+    out[4] = as_h2(u & 0x03000300u);
+    out[5] = as_h2(t & 0x00300030u);
+    out[6] = as_h2(t & 0x00C000C0u);
+    out[7] = as_h2(t & 0x03000300u);
+}
+__device__ __forceinline__ void raw_pair3(uint32_t a, uint32_t b, half2_t out[8])
+{
+    const uint32_t lo = pack_lo16(a, b);              // channels 0..3 (bits 0-11 of each)
+    const uint32_t hi = pack_lo16(a >> 12, b >> 12);  // channels 4..7
+    const uint32_t lt = lo >> 3, ht = hi >> 3;
+    out[0] = as_h2(lo & 0x00070007u);
+    out[1] = as_h2(lo & 0x00380038u);
+    out[2] = as_h2(lo & 0x01C001C0u);
+    out[3] = as_h2(lt & 0x01C001C0u);
+    out[4] = as_h2(hi & 0x00070007u);
+    out[5] = as_h2(hi & 0x00380038u);
+    out[6] = as_h2(hi & 0x01C001C0u);
+    out[7] = as_h2(ht & 0x01C001C0u);
+}
+
 }  // namespace kvq
