@@ -13,10 +13,9 @@
 //    each wave streams 32-token tiles of the split (round robin) and keeps its own
 //    online-softmax state; the waves are merged through LDS at the end.
 //  * tiles reach LDS by direct-to-LDS buffer loads (buffer_load_dwordx4 ... lds) into a
-//    RING-slot ring per wave (RING = 2 or 3): a wave asks for its first two tiles up front
-//    and for tile k+2 once tile k is consumed (2 slots) or has arrived (3 slots), so ~10 KB
-//    per wave is in flight without holding it in VGPRs; the wave waits on vmcnt for
-//    exactly the tile it is about to use.
+//    two-slot ring per wave: a wave asks for its first two tiles up front and for tile k+2
+//    once tile k is consumed, so ~10 KB per wave is in flight without holding it in VGPRs;
+//    the wave waits on vmcnt for exactly the tile it is about to use.
 //  * Q K^T uses v_mfma_f32_16x16x32_f16 with B = the integer codes as fp16 subnormals
 //    (a code masked into mantissa bits k.. of a zero-exponent half is exactly
 //    code * 2^(k-24); one AND per pair of codes) and rows i = 4*head + group of A holding
@@ -52,7 +51,7 @@ namespace {
 #define KVQ_WAVES 4
 #endif
 // LDS of one workgroup: a RING-slot ring of tiles per wave plus small staging arrays
-// (4-bit: ~49 KB with 2 slots, three workgroups per CU; ~69 KB with 3 slots, two per CU).
+// (4-bit: ~49 KB with 2 slots, three workgroups per CU).
 // A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
 template <int TILE_BYTES, int RING, int W>
 struct Smem {
@@ -440,8 +439,11 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
     }
 }
 
+// The inner-grouped kernels are held to 168 VGPRs so that three workgroups (three waves
+// per SIMD) fit on a CU next to their 49 KB of LDS each; the outer-grouped comparison
+// kernel needs more registers and runs two.
 template <int BITS, int NH, int RING, int W, bool PAGED, bool OUTER = false>
-__global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 1 : 3))) void decode_kernel(DecArgs a,
                                                         const int32_t *__restrict__ tbl,
                                                         const int32_t *__restrict__ seq_state)
 {
@@ -652,8 +654,16 @@ __global__ __launch_bounds__(64 * W) void decode_kernel(DecArgs a,
             const int nv = tail_fix(ring + s1 * G::BYTES, my_lo + (k + 1) * kWaves);
             float p8[8];
             load_p8(pbuf + (k & 1) * pstride, n, r, p8);
-            stage_a(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, nxt, alpha, resc, nv);
-            stage_b(p8, cur);
+            if constexpr (OUTER) {
+                stage_a(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, nxt, alpha, resc, nv);
+                stage_b(p8, cur);
+            } else {
+                // P V of tile k first: its operands are ready at the top of the step, so
+                // its MFMAs overlap the unpack and softmax of tile k+1, and fewer values
+                // stay live across the step (the same arithmetic in either order)
+                stage_b(p8, cur);
+                stage_a(ring + s1 * G::BYTES, pbuf + ((k + 1) & 1) * pstride, nxt, alpha, resc, nv);
+            }
             if (resc) rescale_pv(st, alpha);      // tile k's PV is in; tile k+1 moved m
             wait_lgkm0();                                // slot k+1 read, p of tile k+1 written
             if (k + 1 + RING < nt_w) issue(ring + s1 * G::BYTES, my_lo + (k + 1 + RING) * kWaves);
@@ -893,17 +903,11 @@ hipError_t launch_f16_nh(const DecArgs &a, int64_t rows, int chunks, hipStream_t
 #ifndef KVQ_RING
 #define KVQ_RING 2
 #endif
-// Ring depth per wave. Two slots (three workgroups per CU at 4 bits): deeper rings, which
-// keep more tiles in flight per wave but leave fewer waves per CU, measured slower at every
-// grid size tried (e.g. 16.6 us with 7 slots and one workgroup per CU against 12.4 us with
+// Ring depth per wave: two slots (three workgroups per CU). Deeper rings, which keep more
+// tiles in flight per wave but leave fewer waves per CU, measured slower at every grid
+// size tried (e.g. 16.6 us with 7 slots and one workgroup per CU against 12.4 us with
 // 2 slots at 32K tokens), because the first tiles arrive later and one wave per SIMD
 // computes its tiles more slowly.
-inline int ring_depth(int64_t workgroups, int bits)
-{
-    (void)workgroups;
-    (void)bits;
-    return KVQ_RING;
-}
 
 template <int BITS, int NH, int R, bool PAGED = false>
 hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream, const int32_t *tbl = nullptr)
@@ -918,15 +922,7 @@ template <int BITS, int NH>
 hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
 {
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
-    switch (ring_depth(rows * a.S * chunks, BITS)) {
-    case 2: return launch_r<BITS, NH, 2>(a, grid, stream);
-    case 3: return launch_r<BITS, NH, 3>(a, grid, stream);
-    case 4: return launch_r<BITS, NH, 4>(a, grid, stream);
-    case 5: return launch_r<BITS, NH, 5>(a, grid, stream);
-    case 6: return launch_r<BITS, NH, 6>(a, grid, stream);
-    case 7: return launch_r<BITS, NH, 7>(a, grid, stream);
-    default: return launch_r<BITS, NH, (BITS == 4 ? 7 : 8)>(a, grid, stream);   // LDS bound
-    }
+    return launch_r<BITS, NH, KVQ_RING>(a, grid, stream);
 }
 
 template <int BITS>

@@ -376,3 +376,42 @@ def test_outer_calls_reject_hybrid_and_bad_shapes():
                                         0.088, 4, A, A, None) == K.KVQ_ERR_SHAPE
     assert L.kvq_decode_attention_outer(C.byref(f), MIS, 1, 8, 2, A, A, 10240, 128, A, A, 128, 4,
                                         0.088, 4, A, A, None) == K.KVQ_ERR_ALIGN
+
+
+def test_split_rules_match_the_header(tmp_path):
+    """The Python mirrors of the header's inline split rules give the same counts as the
+    header itself, compiled with the host C compiler, over a grid of shapes."""
+    import itertools
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no host C compiler")
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    shapes = list(itertools.product([1, 2, 8, 16, 64], [1, 2, 8, 40], [1, 1024, 4096, 32768, 131072],
+                                    [128, 256]))
+    paged = list(itertools.product([1, 5000, 270520, 4 << 20], [1, 1000, 31712, 131072], [1, 8],
+                                   [128, 256]))
+    src = tmp_path / "rules.c"
+    lines = ['#include <stdio.h>', '#include "kvq.h"', "int main(void) {"]
+    lines += [f'printf("%d\\n", kvq_suggest_splits({B}, {H}, {n}, {cu}));' for B, H, n, cu in shapes]
+    lines += [f'printf("%d\\n", kvq_suggest_splits_paged({t}LL, {m}, {H}, {cu}));'
+              for t, m, H, cu in paged]
+    lines += ["return 0; }"]
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "rules"
+    subprocess.run([cc, "-std=c11", "-D__HIP_PLATFORM_AMD__", "-I", os.path.join(root, "include"),
+                    "-I", "/opt/rocm/include", "-o", str(exe), str(src)], check=True)
+    got = [int(v) for v in subprocess.run([str(exe)], capture_output=True, text=True,
+                                          check=True).stdout.split()]
+    want = [K.suggest_splits(B, H, n, cu) for B, H, n, cu in shapes]
+    want += [K.suggest_splits_paged(t, m, H, cu) for t, m, H, cu in paged]
+    assert got == want
+
+
+def test_split_rule_on_the_workloads():
+    """Three workgroups per CU where splits stay long, two where they would get short."""
+    import synth_inputs as S
+    got = {n: K.suggest_splits(w.B, w.Hkv, w.L) for n, w in S.WORKLOADS.items()}
+    assert got == {"tiny": 4, "llama8b_32k": 64, "batch8_2bit_hybrid": 12,
+                   "long_128k_3bit": 96, "mha_b64_append": 1}
