@@ -16,16 +16,18 @@ namespace {
 
 // Four workgroups of 128 threads per (batch, head), one per quarter of the channels, so
 // that 4 * B * Hq workgroups share the (latency-bound) work. Thread t owns the channels
-// 4 * (t % 8) .. +3 of its quarter for the splits s = t / 8, t / 8 + 16, ...: it first
-// takes the maximum of their lse, then sums w_s o_s and w_s with all loads independent;
-// the sixteen per-thread results of each channel are merged through LDS with the same
-// rule.
+// 4 * (t % 8) .. +3 of its quarter for the splits s = t / 8, t / 8 + 16, ...; it takes them
+// four at a time, issuing the four lse loads and the four partial-output loads together
+// (one memory round trip per four splits: nothing waits for the maximum before the
+// outputs are requested), and keeps a running maximum m with sum w_s o_s and sum w_s
+// relative to it, rescaled when m grows. The sixteen per-thread results of each channel
+// are merged through LDS with the same rule.
 template <bool F16>
 __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
                                                       const float *__restrict__ part_lse, int S,
                                                       void *__restrict__ out)
 {
-    constexpr int kGroups = 16;
+    constexpr int kGroups = 16, kChunk = 4;
     __shared__ float4_t red_o[kGroups][8];
     __shared__ float red_m[kGroups], red_w[kGroups];
     const int64_t bh = blockIdx.x;
@@ -36,18 +38,31 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
     const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) +
                         quarter * 8 + cq;
 
-    float m = -INFINITY;
-#pragma unroll 4
-    for (int s = sg; s < S; s += kGroups) m = fmaxf(m, lse[s]);
-    float ws = 0.0f;
+    float m = -INFINITY, ws = 0.0f;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-    for (int s = sg; s < S; s += kGroups) {
-        const float ls = lse[s];
-        const float4_t x = o[(int64_t)s * (kHeadDim / 4)];
-        const float w = ls == -INFINITY ? 0.0f : __expf(ls - m);
-        acc += w * x;
-        ws += w;
+    for (int s0 = sg; s0 < S; s0 += kGroups * kChunk) {
+        float ls[kChunk];
+        float4_t x[kChunk];
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const int s = s0 + j * kGroups;
+            ls[j] = s < S ? lse[s] : -INFINITY;
+            x[j] = s < S ? o[(int64_t)s * (kHeadDim / 4)] : float4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        float mc = m;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, ls[j]);
+        if (mc == -INFINITY) continue;             // every split so far is empty
+        const float c = m == -INFINITY ? 0.0f : __expf(m - mc);
+        acc *= c;
+        ws *= c;
+#pragma unroll
+        for (int j = 0; j < kChunk; ++j) {
+            const float w = ls[j] == -INFINITY ? 0.0f : __expf(ls[j] - mc);
+            acc += w * x[j];
+            ws += w;
+        }
+        m = mc;
     }
     red_o[sg][cq] = acc;
     if (cq == 0) {

@@ -156,6 +156,39 @@ def test_combine_alone_matches_oracle(oracle_mod):
     assert_close(got, ref)
 
 
+@pytest.mark.parametrize("S_,pattern", [(64, "rising"), (200, "rising"), (200, "falling"),
+                                          (1024, "late"), (129, "random")])
+def test_combine_many_splits(oracle_mod, S_, pattern):
+    """kvq_combine over more splits than one pass of its threads takes (every thread merges
+    several groups of four splits): a rising lse moves each thread's running maximum at every
+    group, a falling one never, and 'late' leaves the first groups of every thread empty."""
+    from gpu_common import DEV, assert_close
+    O = oracle_mod
+    rng = np.random.default_rng(12)
+    B, Hq = 1, 3
+    po = rng.standard_normal((B, Hq, S_, 128))
+    if pattern == "rising":
+        pl = np.broadcast_to(np.linspace(-30.0, 30.0, S_), (B, Hq, S_)).copy()
+    elif pattern == "falling":
+        pl = np.broadcast_to(np.linspace(30.0, -30.0, S_), (B, Hq, S_)).copy()
+    elif pattern == "late":
+        pl = rng.standard_normal((B, Hq, S_)) * 3
+        pl[:, :, : S_ - 100] = -np.inf
+    else:
+        pl = rng.standard_normal((B, Hq, S_)) * 8
+        pl[:, 1, rng.random(S_) < 0.5] = -np.inf
+    po[np.isneginf(pl)] = 0.0
+    ref = O.combine(po, pl)
+    pot = torch.from_numpy(po.astype(np.float32)).to(DEV)
+    plt = torch.from_numpy(pl.astype(np.float32)).to(DEV)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    print(f"[combine many splits] S={S_} {pattern}", flush=True)
+    K.kvq_combine(pot, plt, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
+    got = out.cpu().numpy()
+    assert np.max(np.abs(got - ref)) < 1e-5
+    assert_close(got, ref)
+
+
 def test_decode_fp16_output(oracle_mod):
     from gpu_common import dev, gpu_decode, gpu_quantize
     rng = np.random.default_rng(12)
