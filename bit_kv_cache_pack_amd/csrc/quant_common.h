@@ -4,8 +4,9 @@
 // scale = (max - min) / (2^b - 1) and code = round((x - min) / scale) with a cross-lane
 // min/max (sec. 3.1); 3-bit blog page sec. 2.3 for the clip; InnerQ page
 // ("KV缓存量化技术InnerQ：提升大模型推理效率") sec. 2.2 for the symmetric/asymmetric choice.
-// Every step is one IEEE binary32 operation (no contraction; division correctly rounded),
-// so the bytes equal the CPU definition's.
+// The scales come from IEEE binary32 operations (no contraction; division correctly
+// rounded), and every code equals the one the correctly rounded quotient (x - zero) / scale
+// gives (see code_from_reciprocal), so the bytes equal the CPU definition's.
 #pragma once
 
 #include "kvq_device.h"
@@ -27,6 +28,24 @@ __device__ __forceinline__ float round_half_away(float t)
 #pragma clang fp contract(off)
     const float r = round_half_away_pos(__builtin_fabsf(t));
     return t < 0.0f ? -r : r;
+}
+
+// round_half_away_pos(d / s) for d >= 0, s > 0, computed from r = rcp(s) instead of the
+// correctly rounded division (which costs ~10 instructions and a branch per element).
+// v_rcp_f32 is within 1 ulp of 1/s and the product adds half an ulp, so q = d * r differs
+// from the correctly rounded quotient t by at most 2^-22 * q; rounding q and t to the
+// nearest integer (ties away from zero) then gives the same result unless q lies within
+// that distance of a half-integer. `near` flags the elements within 2^-19 * q (an 8x
+// margin) of one; the caller redoes those with the exact division. s == 0 is passed as
+// r = 0 and yields 0 with `near` false.
+__device__ __forceinline__ float code_from_reciprocal(float d, float r, bool &near)
+{
+#pragma clang fp contract(off)
+    const float q = d * r;
+    const float k = __builtin_truncf(q);
+    const float f = q - k;                                  // exact
+    near = __builtin_fabsf(f - 0.5f) <= q * 0x1p-19f;
+    return f >= 0.5f ? k + 1.0f : k;
 }
 
 // Quantize the group whose 32 fp16 values are spread over a DPP quad (lane j of the quad
@@ -66,11 +85,23 @@ __device__ __forceinline__ void quantize_octet(const u32x4 raw, uint32_t &packed
     const _Float16 zh = (_Float16)mn;     // exact
     const float s = (float)sh, z = (float)zh;
     int code[8];
+    {
+        const float rs = s != 0.0f ? __builtin_amdgcn_rcpf(s) : 0.0f;
+        uint32_t near = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float c = 0.0f;
-        if (s != 0.0f) c = fminf(round_half_away_pos((x[i] - z) / s), (float)N);
-        code[i] = (int)c;
+        for (int i = 0; i < 8; ++i) {
+            bool nr;
+            code[i] = (int)fminf(code_from_reciprocal(x[i] - z, rs, nr), (float)N);
+            near |= (uint32_t)nr << i;
+        }
+        // near a rounding boundary: the correctly rounded quotient decides (rare; a
+        // wave-uniform branch)
+        if (__builtin_amdgcn_ballot_w64(near != 0) != 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                if ((near >> i) & 1u)
+                    code[i] = (int)fminf(round_half_away_pos((x[i] - z) / s), (float)N);
+        }
     }
     out_s = __builtin_bit_cast(uint16_t, sh);
     out_z = __builtin_bit_cast(uint16_t, zh);
@@ -87,12 +118,26 @@ __device__ __forceinline__ void quantize_octet(const u32x4 raw, uint32_t &packed
         const float ss = (float)ssh;
         const float zs = -((float)OFF * ss) + 0.0f;
         const bool eligible = __builtin_fabsf(zs) <= 65504.0f;
+        // k = clamp(round_half_away(x / ss), -QS, QS) = sign(x) * min(QS, round(|x| / ss)),
+        // from the reciprocal as above
         int scode[8];
+        {
+            const float rss = ss != 0.0f ? __builtin_amdgcn_rcpf(ss) : 0.0f;
+            uint32_t near = 0;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float k = 0.0f;
-            if (ss != 0.0f) k = fminf(fmaxf(round_half_away(x[i] / ss), -(float)QS), (float)QS);
-            scode[i] = OFF + (int)k;
+            for (int i = 0; i < 8; ++i) {
+                bool nr;
+                const float k = fminf(code_from_reciprocal(__builtin_fabsf(x[i]), rss, nr), (float)QS);
+                scode[i] = OFF + (int)(x[i] < 0.0f ? -k : k);
+                near |= (uint32_t)nr << i;
+            }
+            if (__builtin_amdgcn_ballot_w64(near != 0) != 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    if ((near >> i) & 1u)
+                        scode[i] = OFF + (int)fminf(fmaxf(round_half_away(x[i] / ss), -(float)QS),
+                                                    (float)QS);
+            }
         }
         // squared errors, balanced pairwise sum in channel order: 8 in-lane, then quad
         float ea[8], es[8];

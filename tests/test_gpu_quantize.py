@@ -47,6 +47,52 @@ def test_quantize_bit_exact_small(oracle_mod, bits, hybrid):
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
 
 
+def _boundary_rows(rng, bits, rows, T):
+    """Groups whose values sit at, and a few fp16 steps around, the half-integer points
+    zero + (k + 1/2) * scale where the code changes, for the scale the group's own min and
+    max give; half of the groups have a zero point so small that x - zero keeps bits far
+    below x's own precision (quotients close to, but not on, a half-integer)."""
+    N = (1 << bits) - 1
+    G = rows * T * 4
+    mag = 2.0 ** rng.uniform(-12, 8, G)
+    z = np.where(rng.random(G) < 0.5, -mag * rng.uniform(0.0, 1.0, G),
+                 rng.choice([-1.0, 1.0], G) * 2.0 ** rng.uniform(-24, -14, G))
+    z16 = z.astype(np.float16)
+    mx16 = (z16.astype(np.float64) + mag).astype(np.float16)
+    # the scale the quantizer derives from this min and max (fp32 arithmetic, then fp16)
+    s = ((mx16.astype(np.float32) - z16.astype(np.float32)) / np.float32(N)).astype(np.float16)
+    k = rng.integers(0, N, (G, 30))
+    tie = z16.astype(np.float64)[:, None] + (k + 0.5) * s.astype(np.float64)[:, None]
+    x = tie.astype(np.float16)
+    for _ in range(4):                               # up to 4 fp16 steps either way
+        step = rng.integers(-1, 2, x.shape)
+        x = np.where(step > 0, np.nextafter(x, np.float16(np.inf)),
+                     np.where(step < 0, np.nextafter(x, np.float16(-np.inf)), x))
+    lo, hi = np.minimum(z16, mx16), np.maximum(z16, mx16)
+    x = np.clip(x, lo[:, None], hi[:, None])
+    grp = np.concatenate([z16[:, None], mx16[:, None], x], axis=1)
+    perm = rng.permuted(np.tile(np.arange(32), (G, 1)), axis=1)
+    grp = np.take_along_axis(grp, perm, axis=1)
+    return np.ascontiguousarray(grp.reshape(rows, T, 128))
+
+
+@pytest.mark.parametrize("bits,hybrid", FORMATS)
+def test_quantize_rounding_boundaries(oracle_mod, bits, hybrid):
+    """Codes of values at and next to the points where rounding changes (the kernel rounds a
+    reciprocal-based quotient and redoes the ones near such a point with the correctly
+    rounded division): bytes equal to the oracle's."""
+    from gpu_common import gpu_quantize
+    O = oracle_mod
+    rng = np.random.default_rng(1200 + bits + 10 * hybrid)
+    src = _boundary_rows(rng, bits, 4, 256)
+    fmt = K.Format(bits, 128, hybrid)
+    print(f"[quantize boundaries] bits={bits} hybrid={hybrid}", flush=True)
+    got = gpu_quantize(fmt, src).cpu().numpy()
+    ref = O.quantize_pack(O.Format(bits, 128, hybrid), src)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+
+
 @pytest.mark.parametrize("bits,hybrid", [(4, False), (2, True), (3, False)])
 def test_quantize_strided_source_and_block_offset(oracle_mod, bits, hybrid):
     """Quantize tokens [128, 384) of a [B][H][L][d] tensor into blocks 2.. of a wider
