@@ -33,19 +33,19 @@ __device__ __forceinline__ float round_half_away(float t)
 // round_half_away_pos(d / s) for d >= 0, s > 0, computed from r = rcp(s) instead of the
 // correctly rounded division (which costs ~10 instructions and a branch per element).
 // v_rcp_f32 is within 1 ulp of 1/s and the product adds half an ulp, so q = d * r differs
-// from the correctly rounded quotient t by at most 2^-22 * q; rounding q and t to the
-// nearest integer (ties away from zero) then gives the same result unless q lies within
-// that distance of a half-integer. `near` flags the elements within 2^-19 * q (an 8x
-// margin) of one; the caller redoes those with the exact division. s == 0 is passed as
-// r = 0 and yields 0 with `near` false.
+// from the correctly rounded quotient t by at most 2^-22 * q. The candidate c = floor(q +
+// 1/2) is accepted when |q - c| < 1/2 - 2^-19 * q: then |t - c| < 1/2, so t rounds to c
+// (whatever rounding q + 1/2 took). q - c is exact (Sterbenz for c >= 1; q itself for
+// c = 0); the threshold's own rounding (<= 2^-26) stays inside the margin for q >= 2^-4 / 7,
+// and below that c = 0 = round(t) anyway. Otherwise `near` is set and the caller redoes the
+// element with the exact division. s == 0 is passed as r = 0 and yields 0, not near.
 __device__ __forceinline__ float code_from_reciprocal(float d, float r, bool &near)
 {
 #pragma clang fp contract(off)
     const float q = d * r;
-    const float k = __builtin_truncf(q);
-    const float f = q - k;                                  // exact
-    near = __builtin_fabsf(f - 0.5f) <= q * 0x1p-19f;
-    return f >= 0.5f ? k + 1.0f : k;
+    const float c = __builtin_floorf(q + 0.5f);
+    near = __builtin_fabsf(q - c) >= __builtin_fmaf(q, -0x1p-19f, 0.5f);
+    return c;
 }
 
 // Quantize the group whose 32 fp16 values are spread over a DPP quad (lane j of the quad
