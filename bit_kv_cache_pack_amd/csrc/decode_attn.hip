@@ -630,8 +630,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
     };
 
     // ---- packed tiles through the ring, software-pipelined ----
-    // Iteration k runs stage A (Q K^T, softmax, p) of tile k+1 next to stage B (P V) of
-    // tile k, so one wave has two independent chains of work. RING tiles are requested up
+    // Iteration k runs stage B (P V) of tile k next to stage A (Q K^T, softmax, p) of
+    // tile k+1, so one wave has two independent chains of work. RING tiles are requested up
     // front; once stage A of tile j has read its slot, tile j + RING is requested into it,
     // so RING - 1 tiles stay in flight behind the one being read.
     float *pbuf = &sm.p[wave][0][0][0];

@@ -14,8 +14,10 @@
 // and the hybrid error sums are quad reductions with DPP; a lane's 8 codes are exactly
 // `bits` bytes of the group's word, so every lane stores its own bytes.
 //
-// Every quantizer step is one IEEE binary32 operation (no contraction: see the pragma;
-// division is the correctly rounded one) so the bytes equal the CPU definition's.
+// The scales are IEEE binary32 operations (no contraction: see the pragma; division is
+// the correctly rounded one) and each code is the one the correctly rounded quotient
+// gives (taken from a reciprocal where that is provably the same, see quant_common.h), so
+// the bytes equal the CPU definition's.
 #include "kvq_internal.h"
 #include "quant_common.h"
 
