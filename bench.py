@@ -439,6 +439,28 @@ def main():
     torch.cuda.synchronize()
     append_ms = e0.elapsed_time(e1) / fl_reps
 
+    # a serving step: the new token into window slot n_res - 1, the decode, the combine; as
+    # three calls, and with the append folded into the decode (kvq_decode_attention_append)
+    def serve3(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_append_residual(kn, kn, krd, vrd, wl.B, wl.Hkv, 128, 128, wl.n_res - 1, stream=sp)
+        decode(i, sp)
+        K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+    def serve2(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_decode_attention_append(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed,
+                                      krd, vrd, 128, wl.n_res, kn, kn, sm, S_, part_o, part_lse,
+                                      stream=sp)
+        K.kvq_combine(part_o, part_lse, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+    serve = None
+    if wl.n_res >= 1:
+        serve3_ms = timed(serve3, args.steps, 5)
+        serve2_ms = timed(serve2, args.steps, 5)
+        serve = {"append_decode_combine_us": round(serve3_ms * 1e3, 3),
+                 "fused_append_decode_combine_us": round(serve2_ms * 1e3, 3)}
+
     # plain device copy as a bandwidth reference (read + write bytes)
     big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
     big2 = torch.empty_like(big)
@@ -476,6 +498,7 @@ def main():
         "append_us": round(append_ms * 1e3, 3),
         "step_us_with_append_and_amortized_flush": round((ms_per_step + append_ms + flush_ms / 128)
                                                          * 1e3, 3),
+        "serving_step": serve,
         "copy_reference_gbps": round(copy_gbps, 1),
         "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L,
                    "bits": wl.bits, "group": 32, "hybrid": wl.hybrid, "n_packed": wl.n_packed,

@@ -702,6 +702,19 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         if constexpr (!OUTER) build_aq(false);
         const uint16_t *kr = a.kres + row * a.res_cap * kHeadDim;
         const uint16_t *vr = a.vres + row * a.res_cap * kHeadDim;
+        // a new token (kvq_decode_attention_append) is window slot n_res - 1: it is read
+        // from k_new / v_new here, and the workgroup of the row's first query heads (first
+        // chunk of the launch that starts at head 0) stores it into the window; every
+        // reader of that slot in these launches reads k_new / v_new instead
+        const int new_slot = a.knew ? n_res_b - 1 : -1;
+        const uint16_t *kn = a.knew ? a.knew + row * kHeadDim : kr;
+        const uint16_t *vn = a.vnew ? a.vnew + row * kHeadDim : vr;
+        if (new_slot >= 0 && a.head_base == 0 && blockIdx.z == 0 && threadIdx.x < 32) {
+            const bool is_v = threadIdx.x >= 16;
+            const int t = threadIdx.x & 15;
+            uint16_t *dst = const_cast<uint16_t *>(is_v ? vr : kr) + (int64_t)new_slot * kHeadDim + 8 * t;
+            *reinterpret_cast<u32x4 *>(dst) = *reinterpret_cast<const u32x4 *>((is_v ? vn : kn) + 8 * t);
+        }
         const int n_rt = (n_res_b + kTile - 1) / kTile;
         for (int rt = wave; rt < n_rt; rt += kWaves) {
             float lg[2], zv[2][4];
@@ -709,7 +722,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
             for (int u = 0; u < 2; ++u) {
                 const int ts = rt * kTile + 16 * u + n;
                 const int tc = ts < n_res_b ? ts : n_res_b - 1;
-                const uint16_t *kt = kr + (int64_t)tc * kHeadDim + 32 * r;
+                const uint16_t *kt = (tc == new_slot ? kn : kr + (int64_t)tc * kHeadDim) + 32 * r;
                 float4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int o = 0; o < 4; ++o)
@@ -725,7 +738,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
             for (int e = 0; e < 8; ++e) {
                 const int ts = rt * kTile + 4 * e + r;
                 const int tc = ts < n_res_b ? ts : n_res_b - 1;
-                vt[e] = *reinterpret_cast<const u32x4 *>(vr + (int64_t)tc * kHeadDim + 8 * n);
+                vt[e] = *reinterpret_cast<const u32x4 *>((tc == new_slot ? vn : vr + (int64_t)tc * kHeadDim) + 8 * n);
             }
             half2_t vpair[4][8];
 #pragma unroll

@@ -32,6 +32,7 @@ struct DecArgs {
     float *part_o, *part_lse;
     int32_t block_bytes, sz_off;
     const float *qnorm;          // key-channel norms [rows][128] q is multiplied by, or null
+    const uint16_t *knew, *vnew; // new token [rows][128] for window slot n_res - 1, or null
     // paged cache (kp / vp are then the pools): block e of sequence b at
     // pool + tbl[b][e] * block_stride + kvh * head_stride; lengths from state[b][0..1]
     int32_t max_blocks;
@@ -269,6 +270,8 @@ inline DecArgs make_dec_args(const DecodeParams &p)
     a.block_bytes = p.block_bytes;
     a.sz_off = p.sz_off;
     a.qnorm = p.qnorm;
+    a.knew = p.knew;
+    a.vnew = p.vnew;
     a.max_blocks = p.max_blocks;
     a.pool_blocks = p.pool_blocks;
     a.block_stride = p.block_stride;

@@ -93,7 +93,8 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
                          const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
                          int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
                          float *part_lse, hipStream_t stream, int kind,
-                         const float *qnorm = nullptr)
+                         const float *qnorm = nullptr, const void *k_new = nullptr,
+                         const void *v_new = nullptr)
 {
     // kind: 0 the MFMA kernel, 1 the VALU comparison kernel, 2 outer-grouped blocks
     if (kind == 2 && fmt && fmt->hybrid) return KVQ_ERR_UNSUPPORTED;
@@ -141,6 +142,8 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
     p.qnorm = qnorm;
+    p.knew = static_cast<const uint16_t *>(k_new);
+    p.vnew = static_cast<const uint16_t *>(v_new);
     if (kind == 2) return launched(kvq::launch_decode_outer(p, stream));
     return launched(kind == 1 ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
 }
@@ -160,6 +163,24 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
                          num_splits, part_o, part_lse, stream, 0);
+}
+
+kvq_status kvq_decode_attention_append(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                       int32_t Hq, int32_t Hkv, const void *k_packed,
+                                       const void *v_packed, int64_t packed_row_stride_bytes,
+                                       int32_t n_packed_tokens, void *k_res_fp16,
+                                       void *v_res_fp16, int32_t res_capacity, int32_t n_res,
+                                       const void *k_new_fp16, const void *v_new_fp16,
+                                       float sm_scale, int32_t num_splits, float *part_o,
+                                       float *part_lse, hipStream_t stream)
+{
+    if (!k_new_fp16 || !v_new_fp16 || !k_res_fp16 || !v_res_fp16) return KVQ_ERR_NULL;
+    if (n_res < 1) return KVQ_ERR_SHAPE;
+    if (!aligned64(k_new_fp16) || !aligned64(v_new_fp16)) return KVQ_ERR_ALIGN;
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, part_o, part_lse, stream, 0, nullptr, k_new_fp16,
+                         v_new_fp16);
 }
 
 kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,

@@ -26,6 +26,9 @@ struct DecodeParams {
     float *part_o, *part_lse;
     int32_t bits, block_bytes, sz_off;
     const float *qnorm;   // key-channel norms [B*Hkv][128] that q is multiplied by, or null
+    // a new token per row [B*Hkv][128] that becomes window slot n_res - 1 (written into the
+    // window by the call and attended from here), or null
+    const uint16_t *knew, *vnew;
     // paged cache only (kp / vp are the pools; n_packed / n_res come from state per sequence)
     const int32_t *tbl;
     int32_t max_blocks;

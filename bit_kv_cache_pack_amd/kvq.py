@@ -26,7 +26,7 @@ EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_k
             "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
             "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale", "kvq_pack_tokens_paged",
             "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
-            "kvq_decode_attention_outer")
+            "kvq_decode_attention_outer", "kvq_decode_attention_append")
 
 
 class KVQError(RuntimeError):
@@ -112,6 +112,8 @@ def lib():
         L.kvq_decode_attention_fp16.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, f32, i32, vp,
                                                 vp, vp]
         L.kvq_combine.argtypes = [vp, vp, i32, i32, i32, i32, vp, i32, vp]
+        L.kvq_decode_attention_append.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp,
+                                                  vp, i32, i32, vp, vp, f32, i32, vp, vp, vp]
         L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
         L.kvq_key_norm.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp]
         L.kvq_channel_scale.argtypes = [vp, i64, i32, i64, i64, i32, vp, i64, i32, vp, i64, i64,
@@ -172,6 +174,21 @@ def kvq_decode_attention(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packe
                                     float(sm_scale), num_splits, _ptr(part_o), _ptr(part_lse),
                                     _stream(stream, q_fp16))
     _check("kvq_decode_attention", st)
+
+
+def kvq_decode_attention_append(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
+                                v_packed, packed_row_stride_bytes: int, n_packed_tokens: int,
+                                k_res_fp16, v_res_fp16, res_capacity: int, n_res: int, k_new_fp16,
+                                v_new_fp16, sm_scale: float, num_splits: int, part_o, part_lse,
+                                stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_append(C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_packed),
+                                           _ptr(v_packed), packed_row_stride_bytes,
+                                           n_packed_tokens, _ptr(k_res_fp16), _ptr(v_res_fp16),
+                                           res_capacity, n_res, _ptr(k_new_fp16),
+                                           _ptr(v_new_fp16), float(sm_scale), num_splits,
+                                           _ptr(part_o), _ptr(part_lse), _stream(stream, q_fp16))
+    _check("kvq_decode_attention_append", st)
 
 
 def kvq_quantize_pack_outer(fmt: Format, src_fp16, n_rows: int, n_tokens: int,

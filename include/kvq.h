@@ -237,6 +237,32 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
                                 float *part_lse, hipStream_t stream);
 
 /*
+ * kvq_decode_attention_append -- kvq_append_residual of one new token into window slot
+ * n_res - 1 followed by kvq_decode_attention, in one launch ([InnerQ] sec. 2.3: the new
+ * token enters the fp16 recent window; the decode then attends to it with the rest). The
+ * workgroups that process the window read the new token from k_new / v_new, and one of them
+ * per (batch, kv-head) stores it into the window, so the window afterwards and the partials
+ * equal those of the two separate calls, bit for bit.
+ *   k_new_fp16, v_new_fp16  fp16 [B][Hkv][head_dim], 64-byte aligned
+ *   k_res_fp16, v_res_fp16  the windows, as for kvq_decode_attention; slot n_res - 1 of
+ *                   every row is written by this call (the caller advances its own count
+ *                   first: n_res here includes the new token)
+ *   n_res           1..res_capacity (KVQ_ERR_SHAPE for 0)
+ *   other arguments, validation and outputs: as kvq_decode_attention. A NULL window or new
+ *   token is KVQ_ERR_NULL. When the window is full before the step, the caller flushes it
+ *   first (kvq_quantize_pack of the 128 window tokens into the next block) and passes
+ *   n_res = 1.
+ */
+kvq_status kvq_decode_attention_append(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                       int32_t Hq, int32_t Hkv, const void *k_packed,
+                                       const void *v_packed, int64_t packed_row_stride_bytes,
+                                       int32_t n_packed_tokens, void *k_res_fp16,
+                                       void *v_res_fp16, int32_t res_capacity, int32_t n_res,
+                                       const void *k_new_fp16, const void *v_new_fp16,
+                                       float sm_scale, int32_t num_splits, float *part_o,
+                                       float *part_lse, hipStream_t stream);
+
+/*
  * ---------------------------------------------------------------------------------
  * Outer-dimension grouping (the comparison the InnerQ page draws: [InnerQ] sec. 1, the
  * conventional KIVI-style grouping along the sequence; sec. 4.1, its timing)

@@ -197,6 +197,33 @@ def test_decode_knorm_rejects(kw, status):
     assert _dec_kn(**kw) == status
 
 
+def _dec_app(fmt=None, q=A, B=1, Hq=8, Hkv=2, kp=A, vp=A, stride=10240, n_packed=128, kr=A,
+             vr=A, cap=128, n_res=4, kn=A, vn=A, sm=0.088, S=4, po=A, pl=A):
+    f = _fmt() if fmt is None else fmt
+    return K.lib().kvq_decode_attention_append(C.byref(f), q, B, Hq, Hkv, kp, vp, stride,
+                                               n_packed, kr, vr, cap, n_res, kn, vn, sm, S, po,
+                                               pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(kn=None), K.KVQ_ERR_NULL),
+    (dict(vn=None), K.KVQ_ERR_NULL),
+    (dict(kr=None), K.KVQ_ERR_NULL),
+    (dict(vr=None), K.KVQ_ERR_NULL),
+    (dict(n_res=0), K.KVQ_ERR_SHAPE),
+    (dict(n_res=129), K.KVQ_ERR_SHAPE),
+    (dict(kn=A + 16), K.KVQ_ERR_ALIGN),
+    (dict(vn=MIS), K.KVQ_ERR_ALIGN),
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(fmt=_fmt(bits=7)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(kp=MIS), K.KVQ_ERR_ALIGN),
+])
+def test_decode_append_rejects(kw, status):
+    assert _dec_app(**kw) == status
+
+
 def _kn(k=A, rows=2, T=300, rs=512 * 128, ts=128, hd=128, norm=A):
     return K.lib().kvq_key_norm(k, rows, T, rs, ts, hd, norm, None)
 

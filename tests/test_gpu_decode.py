@@ -189,6 +189,69 @@ def test_combine_many_splits(oracle_mod, S_, pattern):
     assert_close(got, ref)
 
 
+APPEND_CASES = [
+    # bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S
+    (4, False, 1, 8, 2, 384, 128, 1, 4),       # first token of a fresh window
+    (4, False, 2, 8, 2, 256, 128, 77, 3),
+    (2, True, 1, 32, 2, 128, 128, 128, 5),     # full window, gq 16 (four head chunks)
+    (3, False, 1, 4, 4, 0, 64, 37, 1),         # window only, one split
+    (4, False, 3, 12, 4, 512, 128, 50, 1),     # gq 3 (tail launch), window in split 0
+    (4, False, 1, 10, 2, 256, 100, 100, 2),    # gq 5 (chunk + tail), capacity 100
+    (4, False, 1, 8, 2, 896, 128, 128, 7),
+]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES,
+                         ids=lambda c: "b{}h{}_B{}_{}x{}_P{}_C{}_R{}_S{}".format(*c))
+def test_decode_append_equals_append_then_decode(oracle_mod, case):
+    """kvq_decode_attention_append equals kvq_append_residual into slot n_res - 1 followed by
+    kvq_decode_attention: the same window afterwards and the same partials, bit for bit;
+    and the merged output matches the oracle on the updated cache."""
+    from gpu_common import DEV, assert_close, dev, gpu_quantize
+    O = oracle_mod
+    bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S_ = case
+    rng = np.random.default_rng(300 + n_res)
+    rows = B * Hkv
+    fmt, ofmt = K.Format(bits, 128, hybrid), O.Format(bits, 128, hybrid)
+    q = _f16(rng.standard_normal((B, Hq, 128)))
+    kr = _f16(rng.standard_normal((B, Hkv, cap, 128)))          # slot n_res-1 holds stale data
+    vr = _f16(rng.standard_normal((B, Hkv, cap, 128)))
+    kn = _f16(rng.standard_normal((B, Hkv, 128)) * 2)
+    vn = _f16(rng.standard_normal((B, Hkv, 128)) * 2)
+    print(f"[decode append] case={case}", flush=True)
+    if n_packed:
+        ks = _f16(rng.standard_normal((rows, n_packed, 128)))
+        vs = _f16(rng.standard_normal((rows, n_packed, 128)))
+        kp, vp = gpu_quantize(fmt, ks), gpu_quantize(fmt, vs)
+        kpr, vpr = O.quantize_pack(ofmt, ks), O.quantize_pack(ofmt, vs)
+        assert np.array_equal(kp.cpu().numpy(), kpr) and np.array_equal(vp.cpu().numpy(), vpr)
+        stride = kp.shape[1]
+    else:
+        kp = vp = None
+        kpr = vpr = np.zeros((rows, 0), np.uint8)
+        stride = 0
+    qd, knd, vnd = dev(q), dev(kn), dev(vn)
+    kra, vra, krb, vrb = dev(kr), dev(vr), dev(kr), dev(vr)
+    poa = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pla = torch.empty((B, Hq, S_), dtype=torch.float32, device=DEV)
+    pob, plb = torch.empty_like(poa), torch.empty_like(pla)
+    K.kvq_append_residual(knd, vnd, kra, vra, B, Hkv, 128, cap, n_res - 1)
+    K.kvq_decode_attention(fmt, qd, B, Hq, Hkv, kp, vp, stride, n_packed, kra, vra, cap, n_res,
+                           SM, S_, poa, pla)
+    K.kvq_decode_attention_append(fmt, qd, B, Hq, Hkv, kp, vp, stride, n_packed, krb, vrb, cap,
+                                  n_res, knd, vnd, SM, S_, pob, plb)
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    K.kvq_combine(pob, plb, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
+    torch.cuda.synchronize()
+    assert torch.equal(kra, krb) and torch.equal(vra, vrb), "windows differ"
+    assert torch.equal(pla, plb), "lse differs"
+    assert torch.equal(poa, pob), "partial outputs differ"
+    kr2, vr2 = kr.copy(), vr.copy()
+    kr2[:, :, n_res - 1], vr2[:, :, n_res - 1] = kn, vn
+    ref = O.attention(ofmt, q, Hkv, kpr, vpr, n_packed, kr2, vr2, n_res, sm=SM)
+    assert_close(out.cpu().numpy(), ref, "attention after append")
+
+
 def test_decode_fp16_output(oracle_mod):
     from gpu_common import dev, gpu_decode, gpu_quantize
     rng = np.random.default_rng(12)
