@@ -122,12 +122,15 @@ __device__ __forceinline__ void softmax_a(const float lg[2], const float zv[2][4
     const float tmax = row_max16(fmaxf(lg[0], lg[1]));
     const bool grow = (tmax > st.m + kSlack) || (big_scale && tmax > st.m);
     rescale = __builtin_amdgcn_ballot_w64(grow) != 0;
-    const float mnew = grow ? tmax : st.m;
-    alpha = grow ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.0f;
-    st.m = mnew;
-    st.l *= alpha;
+    alpha = 1.0f;
+    if (rescale) {   // wave-uniform and rare once m has settled; alpha = 1 in every other lane
+        const float mnew = grow ? tmax : st.m;
+        alpha = grow ? __builtin_amdgcn_exp2f(st.m - mnew) : 1.0f;
+        st.m = mnew;
+        st.l *= alpha;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
+        for (int g = 0; g < 4; ++g) st.zacc[g] *= alpha;
+    }
     p0 = __builtin_amdgcn_exp2f(lg[0] - st.m);
     p1 = __builtin_amdgcn_exp2f(lg[1] - st.m);
     st.l += p0 + p1;
