@@ -39,7 +39,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=500)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=2000)
     ap.add_argument("--workload", default="llama8b_32k")
     ap.add_argument("--splits", type=int, default=0, help="0 = the library's suggestion")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -264,6 +264,21 @@ def main():
         torch.cuda.synchronize()
         return t_start.elapsed_time(t_end) / n
 
+    # plain device copy as a bandwidth reference (read + write bytes). It runs before every
+    # timed loop and for ~100 ms (1000 copies of 256 MB): the GPU reaches steady clocks only
+    # after tens of milliseconds of load, so the copies also bring it there.
+    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    for _ in range(1000):
+        big2.copy_(big)
+    t_start.record(stream)
+    for _ in range(10):
+        big2.copy_(big)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * big.numel() * 10 / (t_start.elapsed_time(t_end) * 1e-3) / 1e9
+    del big, big2
+
     # W untimed warm-up steps, then exactly K timed steps back to back (the host enqueues
     # faster than the GPU runs them, so the GPU is never idle waiting for a launch)
     ms_per_step = timed(step, args.steps, args.warmup)
@@ -460,19 +475,6 @@ def main():
         serve2_ms = timed(serve2, args.steps, 5)
         serve = {"append_decode_combine_us": round(serve3_ms * 1e3, 3),
                  "fused_append_decode_combine_us": round(serve2_ms * 1e3, 3)}
-
-    # plain device copy as a bandwidth reference (read + write bytes)
-    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
-    big2 = torch.empty_like(big)
-    for _ in range(3):
-        big2.copy_(big)
-    e0.record(stream)
-    for _ in range(10):
-        big2.copy_(big)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * big.numel() * 10 / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    del big, big2
 
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
     traffic = recorded_traffic(wl.name)
