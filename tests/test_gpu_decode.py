@@ -320,10 +320,12 @@ def test_decode_full_workload(oracle_mod, name):
 
 @pytest.mark.slow
 @pytest.mark.timeout(600)
-def test_append_flush_loop_full(oracle_mod):
+@pytest.mark.parametrize("fused", [False, True], ids=["append_then_decode", "fused_append"])
+def test_append_flush_loop_full(oracle_mod, fused):
     """B64 x 40 heads, L 4096: each step appends one token per sequence; when the 128-slot
     window is full it is quantized into the next packed block first. Checked against the
-    oracle (own packing of the same tokens) at several steps, including both flushes."""
+    oracle (own packing of the same tokens) at several steps, including both flushes. The
+    append is kvq_append_residual + kvq_decode_attention, or kvq_decode_attention_append."""
     from gpu_common import DEV, assert_close, bench_splits, dev, gpu_decode
     O = oracle_mod
     wl = S.WORKLOADS["mha_b64_append"]
@@ -350,6 +352,9 @@ def test_append_flush_loop_full(oracle_mod):
     n_packed, r = wl.n_packed, wl.n_res
     S_ = bench_splits(wl)
     check_at = {1, 2, 64, 128, 129, 256, 257}
+    po = torch.empty((wl.B, wl.Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((wl.B, wl.Hq, S_), dtype=torch.float32, device=DEV)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float32, device=DEV)
     for step in range(1, steps + 1):
         kn, vn, q = S.append_step_inputs(x.rng, wl)
         if r == 128:                            # flush the full window
@@ -361,11 +366,18 @@ def test_append_flush_loop_full(oracle_mod):
             O.quantize_pack(ofmt, vr.reshape(rows, 128, 128), first_block=n_packed // 128, dst=vp_ref)
             n_packed += 128
             r = 0
-        K.kvq_append_residual(dev(kn), dev(vn), krd, vrd, wl.B, wl.Hkv, 128, 128, r)
         kr[:, :, r] = kn
         vr[:, :, r] = vn
-        r += 1
-        out, _, _ = gpu_decode(fmt, dev(q), wl.Hkv, kp, vp, n_packed, krd, vrd, r, S_, sm=SM)
+        if fused:
+            K.kvq_decode_attention_append(fmt, dev(q), wl.B, wl.Hq, wl.Hkv, kp, vp,
+                                          cap_blocks * bb, n_packed, krd, vrd, 128, r + 1,
+                                          dev(kn), dev(vn), SM, S_, po, pl)
+            K.kvq_combine(po, pl, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F32)
+            r += 1
+        else:
+            K.kvq_append_residual(dev(kn), dev(vn), krd, vrd, wl.B, wl.Hkv, 128, 128, r)
+            r += 1
+            out, _, _ = gpu_decode(fmt, dev(q), wl.Hkv, kp, vp, n_packed, krd, vrd, r, S_, sm=SM)
         if step in check_at:
             print(f"[append loop] step {step}: n_packed={n_packed} r={r}", flush=True)
             got = out.cpu().numpy()
