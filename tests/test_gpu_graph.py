@@ -59,6 +59,57 @@ def test_graph_replays_match_eager():
         assert torch.equal(out, ref_out)
 
 
+def test_fused_append_step_graph_replays_match_eager():
+    """kvq_decode_attention_append + kvq_combine captured once; before each replay a new
+    token is copied into the staging buffers the graph reads. Every replay's output and the
+    window afterwards equal the same calls run eagerly on a copy of the cache."""
+    from gpu_common import DEV, dev, gpu_quantize
+    wl = S.WORKLOADS["tiny"]
+    x = S.make_inputs(wl)
+    rows = wl.B * wl.Hkv
+    fmt = K.Format(wl.bits)
+    kps, vps = x.packed_src()
+    kp = gpu_quantize(fmt, np.ascontiguousarray(kps.reshape(rows, wl.n_packed, 128)))
+    vp = gpu_quantize(fmt, np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128)))
+    kr0, vr0 = x.residual()
+    krg, vrg, kre, vre = dev(kr0), dev(vr0), dev(kr0), dev(vr0)
+    q = dev(x.q)
+    S_, n_res = 4, wl.n_res
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+    kn = torch.zeros((wl.B, wl.Hkv, 128), dtype=torch.float16, device=DEV)
+    vn = torch.zeros_like(kn)
+    po = torch.empty((wl.B, wl.Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pl = torch.empty((wl.B, wl.Hq, S_), dtype=torch.float32, device=DEV)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device=DEV)
+    poe, ple, oute = torch.empty_like(po), torch.empty_like(pl), torch.empty_like(out)
+
+    def step(kr, vr, po_, pl_, out_, sp):
+        K.kvq_decode_attention_append(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, kp.shape[1],
+                                      wl.n_packed, kr, vr, 128, n_res, kn, vn, sm, S_, po_, pl_,
+                                      stream=sp)
+        K.kvq_combine(po_, pl_, wl.B, wl.Hq, 128, S_, out_, K.KVQ_OUT_F16, stream=sp)
+
+    print("[graph fused append] capture", flush=True)
+    side = torch.cuda.Stream(DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        step(krg, vrg, po, pl, out, torch.cuda.current_stream(DEV).cuda_stream)
+    rng = np.random.default_rng(9)
+    for rep in range(5):
+        kn.copy_(dev(rng.standard_normal((wl.B, wl.Hkv, 128)).astype(np.float16)))
+        vn.copy_(dev(rng.standard_normal((wl.B, wl.Hkv, 128)).astype(np.float16)))
+        out.fill_(0)
+        torch.cuda.synchronize()
+        print(f"[graph fused append] replay {rep}", flush=True)
+        g.replay()
+        step(kre, vre, poe, ple, oute, None)          # the same step, eagerly, on the copy
+        torch.cuda.synchronize()
+        assert torch.equal(out, oute), f"replay {rep}: output differs"
+        assert torch.equal(po, poe) and torch.equal(pl, ple), f"replay {rep}: partials differ"
+        assert torch.equal(krg, kre) and torch.equal(vrg, vre), f"replay {rep}: window differs"
+        assert torch.equal(krg[:, :, n_res - 1], kn), f"replay {rep}: new token not stored"
+
+
 def test_paged_step_graph_replays_match_eager():
     """One paged serving step (kvq_append_evict + kvq_decode_attention_paged + kvq_combine)
     captured once and replayed for 40 steps, the new tokens and q copied in before each
