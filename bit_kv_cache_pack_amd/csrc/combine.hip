@@ -14,22 +14,21 @@
 namespace kvq {
 namespace {
 
-// Four workgroups of 128 threads per (batch, head), one per quarter of the channels, so
-// that 4 * B * Hq workgroups share the (latency-bound) work. Thread t owns the channels
-// 4 * (t % 8) .. +3 of its quarter for the splits s = t / 8, t / 8 + 16, ...; it takes them
-// four at a time, issuing the four lse loads and the four partial-output loads together
-// (one memory round trip per four splits: nothing waits for the maximum before the
-// outputs are requested), and keeps a running maximum m with sum w_s o_s and sum w_s
-// relative to it, rescaled when m grows. The sixteen per-thread results of each channel
-// are merged through LDS with the same rule.
+// Four one-wave workgroups per (batch, head), one per quarter of the channels, so that
+// 4 * B * Hq workgroups share the (latency-bound) work and no workgroup barrier is needed.
+// Lane t owns the channels 4 * (t % 8) .. +3 of its quarter for the splits s = t / 8,
+// t / 8 + 8, ...; it takes them eight at a time, issuing the eight lse loads and the eight
+// partial-output loads together (one memory round trip per 64 splits: nothing waits for
+// the maximum before the outputs are requested), and keeps a running maximum m with
+// sum w_s o_s and sum w_s relative to it, rescaled when m grows. The eight lanes that own
+// the same four channels then merge their (m, sum w o, sum w) with the same rule over a
+// butterfly of lane exchanges (xor 8, 16, 32).
 template <bool F16>
-__global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ part_o,
-                                                      const float *__restrict__ part_lse, int S,
-                                                      void *__restrict__ out)
+__global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ part_o,
+                                                     const float *__restrict__ part_lse, int S,
+                                                     void *__restrict__ out)
 {
-    constexpr int kGroups = 16, kChunk = 4;
-    __shared__ float4_t red_o[kGroups][8];
-    __shared__ float red_m[kGroups], red_w[kGroups];
+    constexpr int kGroups = 8, kChunk = 8;
     const int64_t bh = blockIdx.x;
     const int quarter = blockIdx.y;
     const int t = threadIdx.x;
@@ -37,7 +36,6 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
     const float *lse = part_lse + bh * S;
     const float4_t *o = reinterpret_cast<const float4_t *>(part_o + bh * (int64_t)S * kHeadDim) +
                         quarter * 8 + cq;
-
     float m = -INFINITY, ws = 0.0f;
     float4_t acc = {0.f, 0.f, 0.f, 0.f};
     for (int s0 = sg; s0 < S; s0 += kGroups * kChunk) {
@@ -52,7 +50,7 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
         float mc = m;
 #pragma unroll
         for (int j = 0; j < kChunk; ++j) mc = fmaxf(mc, ls[j]);
-        if (mc == -INFINITY) continue;             // every split so far is empty
+        if (mc == -INFINITY) continue;
         const float c = m == -INFINITY ? 0.0f : __expf(m - mc);
         acc *= c;
         ws *= c;
@@ -64,25 +62,23 @@ __global__ __launch_bounds__(128) void combine_kernel(const float *__restrict__ 
         }
         m = mc;
     }
-    red_o[sg][cq] = acc;
-    if (cq == 0) {
-        red_m[sg] = m;
-        red_w[sg] = ws;
+    // butterfly over the eight split groups (lanes cq, cq + 8, ..., cq + 56)
+#pragma unroll
+    for (int d = 8; d < 64; d <<= 1) {
+        const float m2 = __shfl_xor(m, d);
+        const float w2 = __shfl_xor(ws, d);
+        float4_t a2;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) a2[k] = __shfl_xor(acc[k], d);
+        const float M = fmaxf(m, m2);
+        const float c1 = m == -INFINITY ? 0.0f : __expf(m - M);
+        const float c2 = m2 == -INFINITY ? 0.0f : __expf(m2 - M);
+        acc = c1 * acc + c2 * a2;
+        ws = c1 * ws + c2 * w2;
+        m = M;
     }
-    __syncthreads();
     if (t < 8) {
-        float M = red_m[0];
-#pragma unroll
-        for (int k = 1; k < kGroups; ++k) M = fmaxf(M, red_m[k]);
-        float4_t tot = {0.f, 0.f, 0.f, 0.f};
-        float W = 0.0f;
-#pragma unroll
-        for (int k = 0; k < kGroups; ++k) {
-            const float c = red_m[k] == -INFINITY ? 0.0f : __expf(red_m[k] - M);
-            tot += c * red_o[k][t];
-            W += c * red_w[k];
-        }
-        const float4_t r = tot / W;
+        const float4_t r = acc / ws;
         const int64_t idx = bh * (kHeadDim / 4) + quarter * 8 + t;
         if (F16) {
             typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
@@ -117,10 +113,10 @@ hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B,
 {
     const dim3 grid((uint32_t)((int64_t)B * Hq), 4);
     if (out_f16)
-        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(128), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<true>, grid, dim3(64), 0, stream, part_o, part_lse,
                            num_splits, out);
     else
-        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(128), 0, stream, part_o, part_lse,
+        hipLaunchKernelGGL(combine_kernel<false>, grid, dim3(64), 0, stream, part_o, part_lse,
                            num_splits, out);
     return hipGetLastError();
 }
