@@ -329,7 +329,7 @@ def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
     rows = B * Hkv
     tiles = n_tokens // 32
     want = (3 * cu_count + rows - 1) // rows
-    if tiles < 32 * want:
+    if tiles < 64 * want:
         want = (2 * cu_count + rows - 1) // rows
     cap = tiles // 8
     return int(max(1, min(256, min(want, cap))))

@@ -142,16 +142,16 @@ static inline int64_t kvq_block_bytes(const kvq_format *f)
 }
 /* A split count for decode on `cu_count` CUs: enough splits that B*Hkv*S workgroups give
    three workgroups per CU (the decode kernel's registers and LDS allow three) while each
-   split keeps at least 32 packed 32-token tiles, else two per CU (shorter splits pay the
-   per-workgroup start and merge too often: two measured best at 32K tokens x 8 kv-heads,
-   three at 128K x 8 and at 32K x 64), and never fewer than 8 tiles per split. */
+   split keeps at least 64 packed 32-token tiles, else two per CU (shorter splits pay the
+   per-workgroup start and merge too often: two measured best at 32K tokens x 8 kv-heads
+   and at 128K x 8, three at 32K x 64), and never fewer than 8 tiles per split. */
 static inline int32_t kvq_suggest_splits(int32_t B, int32_t Hkv, int32_t n_tokens,
                                          int32_t cu_count)
 {
     int64_t rows = (int64_t)B * Hkv;
     int64_t tiles = n_tokens / 32;
     int64_t want = (3LL * cu_count + rows - 1) / rows;
-    if (tiles < 32 * want) want = (2LL * cu_count + rows - 1) / rows;
+    if (tiles < 64 * want) want = (2LL * cu_count + rows - 1) / rows;
     int64_t cap = tiles / 8;
     int64_t s = want < cap ? want : cap;
     if (s < 1) s = 1;

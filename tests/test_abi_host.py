@@ -441,4 +441,4 @@ def test_split_rule_on_the_workloads():
     import synth_inputs as S
     got = {n: K.suggest_splits(w.B, w.Hkv, w.L) for n, w in S.WORKLOADS.items()}
     assert got == {"tiny": 4, "llama8b_32k": 64, "batch8_2bit_hybrid": 12,
-                   "long_128k_3bit": 96, "mha_b64_append": 1}
+                   "long_128k_3bit": 64, "mha_b64_append": 1}
