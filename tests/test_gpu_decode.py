@@ -189,6 +189,35 @@ def test_combine_many_splits(oracle_mod, S_, pattern):
     assert_close(got, ref)
 
 
+def _random_cases(n, seed=2024):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        bits = int(rng.choice([2, 3, 4]))
+        hybrid = bool(rng.random() < 0.3)
+        Hkv = int(rng.choice([1, 2, 3, 4]))
+        gq = int(rng.choice([1, 2, 3, 4, 5, 8, 16]))
+        B = int(rng.integers(1, 4))
+        n_packed = 128 * int(rng.integers(0, 9))
+        cap = int(rng.choice([32, 64, 100, 128]))
+        n_res = int(rng.integers(0 if n_packed else 1, cap + 1))
+        S_ = int(rng.choice([1, 2, 3, 5, 8, 16, 33]))
+        out.append((i, bits, hybrid, B, gq * Hkv, Hkv, n_packed, n_res, cap, S_))
+    return out
+
+
+@pytest.mark.parametrize("case", _random_cases(24), ids=lambda c: f"r{c[0]}")
+def test_decode_random_shapes(oracle_mod, case):
+    """Seeded random shapes (bits, hybrid, batch, GQA 1-16, packed length, window fill and
+    capacity, split count): output and partials against the oracle; where the window is not
+    empty, also through kvq_decode_attention_append (bit-identical to append + decode)."""
+    i, bits, hybrid, B, Hq, Hkv, n_packed, n_res, cap, S_ = case
+    _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, seed=500 + i, cap=cap)
+    if n_res >= 1:
+        test_decode_append_equals_append_then_decode(
+            oracle_mod, (bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S_))
+
+
 APPEND_CASES = [
     # bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S
     (4, False, 1, 8, 2, 384, 128, 1, 4),       # first token of a fresh window
