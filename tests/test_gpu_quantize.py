@@ -93,6 +93,39 @@ def test_quantize_rounding_boundaries(oracle_mod, bits, hybrid):
     assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
 
 
+def _random_quant_cases(n, seed=77):
+    rng = np.random.default_rng(seed)
+    kinds = ["normal", "t5", "wide", "tiny", "offset", "few_levels", "ternary"]
+    return [(i, int(rng.choice([2, 3, 4])), bool(rng.random() < 0.4),
+             str(rng.choice(kinds)), int(rng.integers(1, 6)), 128 * int(rng.integers(1, 5)),
+             int(rng.integers(0, 3)), int(rng.integers(0, 3))) for i in range(n)]
+
+
+@pytest.mark.parametrize("case", _random_quant_cases(12), ids=lambda c: f"r{c[0]}_{c[3]}")
+def test_quantize_random_shapes(oracle_mod, case):
+    """Seeded random formats, value shapes, row counts, token counts, padded token strides and
+    block offsets: packed bytes equal to the oracle's."""
+    from gpu_common import DEV, dev
+    O = oracle_mod
+    i, bits, hybrid, kind, rows, T, pad, fb = case
+    rng = np.random.default_rng(1300 + i)
+    tok_stride = 128 + 8 * pad                        # padded token rows (16-byte multiples)
+    x = S.random_groups(rng, rows * T * 4, kind).reshape(rows, T, 128)
+    src = np.zeros((rows, T, tok_stride), np.float16)
+    src[:, :, :128] = x
+    fmt, ofmt = K.Format(bits, 128, hybrid), O.Format(bits, 128, hybrid)
+    bb = fmt.block_bytes
+    cap = fb + T // 128
+    print(f"[quantize random] case={case}", flush=True)
+    dst = torch.zeros((rows, cap * bb), dtype=torch.uint8, device=DEV)
+    K.kvq_quantize_pack(fmt, dev(src), rows, T, T * tok_stride, tok_stride, dst, cap * bb, fb)
+    ref = O.quantize_pack(ofmt, np.ascontiguousarray(x), n_blocks_capacity=cap, first_block=fb)
+    got = dst.cpu().numpy()
+    bad = np.flatnonzero(got[:, fb * bb:] != ref[:, fb * bb:])
+    assert bad.size == 0, f"{bad.size} bytes differ, first at {bad[:8]}"
+    assert not got[:, :fb * bb].any(), "bytes before the first block were written"
+
+
 @pytest.mark.parametrize("bits,hybrid", [(4, False), (2, True), (3, False)])
 def test_quantize_strided_source_and_block_offset(oracle_mod, bits, hybrid):
     """Quantize tokens [128, 384) of a [B][H][L][d] tensor into blocks 2.. of a wider
