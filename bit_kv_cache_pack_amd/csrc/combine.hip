@@ -78,7 +78,8 @@ __global__ __launch_bounds__(64) void combine_kernel(const float *__restrict__ p
         m = M;
     }
     if (t < 8) {
-        const float4_t r = acc / ws;
+        // a (b, h) whose splits are all empty attended no token: its output is 0
+        const float4_t r = ws > 0.0f ? acc / ws : float4_t{0.f, 0.f, 0.f, 0.f};
         const int64_t idx = bh * (kHeadDim / 4) + quarter * 8 + t;
         if (F16) {
             typedef _Float16 half4_t __attribute__((ext_vector_type(4)));

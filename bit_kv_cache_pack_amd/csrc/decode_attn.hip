@@ -59,6 +59,7 @@ struct Smem {
     alignas(16) uint16_t q[W][4][kHeadDim];            // per-wave copy of the chunk's q
     alignas(16) float p[W][2][4][kTile];      // p of head h, token t of tiles 2j and 2j+1
     alignas(16) float ml[W][4][2];
+    uint32_t flag;                            // last-arrival flag of the fused split merge
     __device__ __forceinline__ float *mo(int w) { return reinterpret_cast<float *>(&ring[w][0][0]); }
 };
 
@@ -381,13 +382,13 @@ __device__ __forceinline__ void stage_b_outer(const float p8[8], const PVInO &pv
     }
 }
 
-// Merge the W waves' states of one workgroup through LDS (sm.mo, sm.ml) and write the
-// split's partials: part_o (normalised) and part_lse (natural log) of the chunk's NH heads,
-// query head hq0 + h. Every wave of the workgroup must call it.
+// Merge the W waves' states of one workgroup through LDS (sm.mo, sm.ml). Thread t ends up
+// with head h = t / 64 of the chunk and channels d, d + 1 (d = 2 * (t % 64)): the workgroup's
+// normalised output o and its log-sum-exp in the exp2 domain (-inf, with o = 0, when the
+// workgroup attended no token). Every wave of the workgroup must call it.
 template <int NH, int W, class SM>
-__device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wave, int n, int r,
-                                            float *part_o, float *part_lse, int64_t hq0, int S,
-                                            int split)
+__device__ __forceinline__ void merge_waves(SM &sm, const WaveState &st, int wave, int n, int r,
+                                            float &v0, float &v1, float &lse2)
 {
     const float lsum = row_sum16(st.l);
     float zr[4];
@@ -413,6 +414,9 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
     __syncthreads();
     const int h = threadIdx.x >> 6;       // 4 heads x 64 threads x 2 channels
     const int d = (threadIdx.x & 63) * 2;
+    v0 = 0.f;
+    v1 = 0.f;
+    lse2 = -INFINITY;
     if (h < NH) {
         float Mx = -INFINITY;
 #pragma unroll
@@ -427,25 +431,181 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
                 o1 += e * sm.mo(w)[h * kHeadDim + d + 1];
             }
         }
-        const int64_t hq = hq0 + h;
-        const int64_t ob = (hq * S + split) * kHeadDim + d;
-        float v0 = 0.f, v1 = 0.f, lse = -INFINITY;
         if (L > 0.f) {
             const float inv = 1.0f / L;
             v0 = o0 * inv;
             v1 = o1 * inv;
-            lse = (Mx + __log2f(L)) * 0.69314718055994531f;
+            lse2 = Mx + __log2f(L);
         }
+    }
+}
+
+// The split's partials: part_o (normalised) and part_lse (natural log) of the chunk's NH
+// heads, query head hq0 + h.
+template <int NH, int W, class SM>
+__device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wave, int n, int r,
+                                            float *part_o, float *part_lse, int64_t hq0, int S,
+                                            int split)
+{
+    float v0, v1, lse2;
+    merge_waves<NH, W>(sm, st, wave, n, r, v0, v1, lse2);
+    const int h = threadIdx.x >> 6;
+    const int d = (threadIdx.x & 63) * 2;
+    if (h < NH) {
+        const int64_t hq = hq0 + h;
+        const int64_t ob = (hq * S + split) * kHeadDim + d;
         part_o[ob] = v0;
         part_o[ob + 1] = v1;
-        if (d == 0) part_lse[hq * S + split] = lse;
+        if (d == 0) part_lse[hq * S + split] = lse2 == -INFINITY ? -INFINITY : lse2 * 0.69314718055994531f;
+    }
+}
+
+// ---------------------------------------------------------------------------------------
+// Split merge inside the decode launch (kvq_decode_attention_fused). The splits of one group
+// (a row's head chunk) form a tree of fan-in 8: every workgroup stores its record (the
+// output of the chunk's heads and their log-sum-exp), then counts itself in its parent's
+// counter; the last of a parent's (up to 8) children merges their records into the parent's
+// record and goes up one level, and the last one at the top writes the output. Nobody waits
+// for anybody, so the launch drains however its workgroups are scheduled.
+// Records and counters are read and written with device-scope coherent accesses (the sc1
+// cache policy: the L2 of each XCD passes them through), and a workgroup counts itself only
+// after its record stores have completed (s_waitcnt vmcnt(0)), so the merging workgroup,
+// which issues its loads after its counter update returned, sees every child's record
+// wherever the children ran.
+// Workspace: slots of kRecFloats words, kvq::fused_records(S) per group (a row's head
+// chunk); for S = 1 none (the workgroup writes the output directly). A slot holds a record
+// (4 heads x 128 outputs, then the 4 log2-domain log-sum-exps) and, in word kCtrWord, the
+// counter of the parent whose first child the record is. Records never write that word and
+// the workgroup that completes a parent puts its counter back to zero, so every counter
+// word is zero again when a launch ends, whatever the shapes of the launches that share
+// the workspace: the slot grid is the same for all of them.
+constexpr int kRecFloats = 520;
+constexpr int kCtrWord = 516;
+constexpr int kScDevice = 16;            // sc1: device-scope coherent load / store
+
+__device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t rr, int rec, float v0, float v1,
+                                          float lse2)
+{
+    const int h = threadIdx.x >> 6;
+    const int d = (threadIdx.x & 63) * 2;
+    const u32x2 v = {__float_as_uint(v0), __float_as_uint(v1)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
+                                          0, kScDevice);
+    if (d == 0)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lse2), rr,
+                                              (uint32_t)((rec * kRecFloats + 4 * kHeadDim + h) * 4), 0,
+                                              kScDevice);
+}
+
+// merge records first .. first + cnt - 1 (cnt <= 8) into (v0, v1, lse2)
+__device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, int cnt, float &v0,
+                                          float &v1, float &lse2)
+{
+    const int h = threadIdx.x >> 6;
+    const int d = (threadIdx.x & 63) * 2;
+    u32x2 x[8];
+    uint32_t lb[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const int rec = first + (j < cnt ? j : 0);
+        x[j] = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
+                                                    0, kScDevice);
+        lb[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)((rec * kRecFloats + 4 * kHeadDim + h) * 4),
+                                                     0, kScDevice);
+    }
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+        if (j < cnt) M = fmaxf(M, __uint_as_float(lb[j]));
+    float a0 = 0.f, a1 = 0.f, ws = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            if (j < cnt) {
+                const float w = __builtin_amdgcn_exp2f(__uint_as_float(lb[j]) - M);
+                a0 += w * __uint_as_float(x[j][0]);
+                a1 += w * __uint_as_float(x[j][1]);
+                ws += w;
+            }
+        }
+    }
+    if (ws > 0.f) {
+        const float inv = 1.0f / ws;
+        v0 = a0 * inv;
+        v1 = a1 * inv;
+        lse2 = M + __log2f(ws);
+    } else {
+        v0 = 0.f;
+        v1 = 0.f;
+        lse2 = -INFINITY;
+    }
+}
+
+template <int NH>
+__device__ __forceinline__ void out_store(const DecArgs &a, int64_t hq0, float v0, float v1)
+{
+    const int h = threadIdx.x >> 6;
+    const int d = (threadIdx.x & 63) * 2;
+    if (h >= NH) return;
+    const int64_t o = (hq0 + h) * kHeadDim + d;
+    if (a.out_f16) {
+        const half2_t hv = {(_Float16)v0, (_Float16)v1};
+        *reinterpret_cast<half2_t *>(static_cast<uint16_t *>(a.out) + o) = hv;
+    } else {
+        *reinterpret_cast<float2 *>(static_cast<float *>(a.out) + o) = float2{v0, v1};
+    }
+}
+
+template <int NH, int W, class SM>
+__device__ __forceinline__ void merge_fused(SM &sm, const WaveState &st, int wave, int n, int r,
+                                            const DecArgs &a, int64_t group, int64_t hq0, int split)
+{
+    float v0, v1, lse2;
+    merge_waves<NH, W>(sm, st, wave, n, r, v0, v1, lse2);
+    if (a.S == 1) {
+        out_store<NH>(a, hq0, v0, v1);
+        return;
+    }
+    float *recs = static_cast<float *>(a.ws) + group * a.rec_per_group * kRecFloats;
+    const __amdgpu_buffer_rsrc_t rr = __builtin_amdgcn_make_buffer_rsrc(
+        recs, 0, a.rec_per_group * kRecFloats * 4, kRsrcWord3);
+    int n_lvl = a.S, idx = split, rec0 = 0;
+    rec_store(rr, idx, v0, v1, lse2);
+    for (;;) {
+        const int parent = idx >> 3, first = parent << 3;
+        const int cnt = n_lvl - first < 8 ? n_lvl - first : 8;
+        const int n_up = (n_lvl + 7) >> 3;
+        if (cnt > 1) {
+            asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this record is stored
+            __syncthreads();
+            if (threadIdx.x == 0) {
+                uint32_t *c = reinterpret_cast<uint32_t *>(recs + (int64_t)(rec0 + first) * kRecFloats) +
+                              kCtrWord;
+                const uint32_t old = __hip_atomic_fetch_add(c, 1u, __ATOMIC_RELAXED,
+                                                            __HIP_MEMORY_SCOPE_AGENT);
+                const uint32_t last = old == (uint32_t)(cnt - 1);
+                if (last) __hip_atomic_store(c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sm.flag = last;
+            }
+            __syncthreads();
+            if (!sm.flag) return;
+            rec_merge(rr, rec0 + first, cnt, v0, v1, lse2);
+        }
+        if (n_up == 1) {
+            out_store<NH>(a, hq0, v0, v1);
+            return;
+        }
+        rec0 += n_lvl;
+        idx = parent;
+        n_lvl = n_up;
+        rec_store(rr, rec0 + idx, v0, v1, lse2);
     }
 }
 
 // The inner-grouped kernels are held to 168 VGPRs so that three workgroups (three waves
 // per SIMD) fit on a CU next to their 49 KB of LDS each; the outer-grouped comparison
 // kernel needs more registers and runs two.
-template <int BITS, int NH, int RING, int W, bool PAGED, bool OUTER = false>
+template <int BITS, int NH, int RING, int W, bool PAGED, bool OUTER = false, bool FUSED = false>
 __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 1 : 3))) void decode_kernel(DecArgs a,
                                                         const int32_t *__restrict__ tbl,
                                                         const int32_t *__restrict__ seq_state)
@@ -767,8 +927,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         }
     }
 
-    // ---- merge the waves, write this split's partials ----
-    merge_store<NH, W>(sm, st, wave, n, r, a.part_o, a.part_lse, (int64_t)b * a.Hq + h0, a.S, split);
+    // ---- merge the waves; write this split's partials, or merge the splits here ----
+    if constexpr (FUSED)
+        merge_fused<NH, W>(sm, st, wave, n, r, a, row * a.n_chunks + (a.head_base >> 2) + blockIdx.z,
+                           (int64_t)b * a.Hq + h0, split);
+    else
+        merge_store<NH, W>(sm, st, wave, n, r, a.part_o, a.part_lse, (int64_t)b * a.Hq + h0, a.S,
+                           split);
 }
 
 // ---------------------------------------------------------------------------------------
@@ -788,8 +953,8 @@ __device__ __forceinline__ void issue_tile_f16(__amdgpu_buffer_rsrc_t rk, __amdg
     const uint32_t base = (uint32_t)tile * (kTile * kF16TokB);
 #pragma unroll
     for (int k = 0; k < kTile * kF16TokB / 1024; ++k) {
-        dma(rk, slot + 1024 * k, base + 1024 * k + lane * 16, 16);
-        dma(rv, slot + kTile * kF16TokB + 1024 * k, base + 1024 * k + lane * 16, 16);
+        dma_nt(rk, slot + 1024 * k, base + 1024 * k + lane * 16);
+        dma_nt(rv, slot + kTile * kF16TokB + 1024 * k, base + 1024 * k + lane * 16);
     }
 }
 
@@ -925,58 +1090,58 @@ hipError_t launch_f16_nh(const DecArgs &a, int64_t rows, int chunks, hipStream_t
 // 2 slots at 32K tokens), because the first tiles arrive later and one wave per SIMD
 // computes its tiles more slowly.
 
-template <int BITS, int NH, int R, bool PAGED = false>
+template <int BITS, int NH, int R, bool PAGED = false, bool FUSED = false>
 hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream, const int32_t *tbl = nullptr)
 {
     constexpr int W = KVQ_WAVES;
-    hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W, PAGED>), grid, dim3(64 * W), 0, stream, a,
-                       tbl, a.state);
+    hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W, PAGED, false, FUSED>), grid, dim3(64 * W), 0,
+                       stream, a, tbl, a.state);
     return hipGetLastError();
 }
 
-template <int BITS, int NH>
-hipError_t launch_t(const DecArgs &a, int64_t rows, int chunks, hipStream_t stream)
+template <int BITS, bool PAGED, bool FUSED>
+hipError_t launch_bits(const DecArgs &a, const int32_t *tbl, int nh, int64_t rows, int chunks,
+                       hipStream_t stream)
 {
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
-    return launch_r<BITS, NH, KVQ_RING>(a, grid, stream);
-}
-
-template <int BITS>
-hipError_t launch_bits(const DecArgs &a, int nh, int64_t rows, int chunks, hipStream_t stream)
-{
     switch (nh) {
-    case 1: return launch_t<BITS, 1>(a, rows, chunks, stream);
-    case 2: return launch_t<BITS, 2>(a, rows, chunks, stream);
-    case 3: return launch_t<BITS, 3>(a, rows, chunks, stream);
-    case 4: return launch_t<BITS, 4>(a, rows, chunks, stream);
+    case 1: return launch_r<BITS, 1, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
+    case 2: return launch_r<BITS, 2, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
+    case 3: return launch_r<BITS, 3, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
+    case 4: return launch_r<BITS, 4, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
     default: return hipErrorInvalidValue;
     }
 }
 
-// paged cache: the default ring depth only
-template <int BITS>
-hipError_t launch_paged_bits(const DecArgs &a, const int32_t *tbl, int nh, int64_t rows,
-                             int chunks, hipStream_t stream)
-{
-    const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
-    switch (nh) {
-    case 1: return launch_r<BITS, 1, KVQ_RING, true>(a, grid, stream, tbl);
-    case 2: return launch_r<BITS, 2, KVQ_RING, true>(a, grid, stream, tbl);
-    case 3: return launch_r<BITS, 3, KVQ_RING, true>(a, grid, stream, tbl);
-    case 4: return launch_r<BITS, 4, KVQ_RING, true>(a, grid, stream, tbl);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_paged_nh(const DecArgs &a, const int32_t *tbl, int bits, int nh, int64_t rows,
-                           int chunks, hipStream_t stream)
+template <bool PAGED, bool FUSED>
+hipError_t launch_nh(const DecArgs &a, const int32_t *tbl, int bits, int nh, int64_t rows,
+                     int chunks, hipStream_t stream)
 {
     switch (bits) {
-    case 2: return launch_paged_bits<2>(a, tbl, nh, rows, chunks, stream);
-    case 3: return launch_paged_bits<3>(a, tbl, nh, rows, chunks, stream);
-    case 4: return launch_paged_bits<4>(a, tbl, nh, rows, chunks, stream);
+    case 2: return launch_bits<2, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
+    case 3: return launch_bits<3, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
+    case 4: return launch_bits<4, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+// the launches of one decode call: the full 4-head chunks of every row, then (gq % 4 != 0)
+// one launch for the remaining heads of every row
+template <bool PAGED, bool FUSED>
+hipError_t launch_chunks(DecArgs a, const int32_t *tbl, int bits, int64_t rows, hipStream_t stream)
+{
+    const int full = a.gq / 4, tail = a.gq % 4;
+    hipError_t e = hipSuccess;
+    if (full > 0) {
+        a.head_base = 0;
+        e = launch_nh<PAGED, FUSED>(a, tbl, bits, 4, rows, full, stream);
+        if (e != hipSuccess) return e;
+    }
+    if (tail > 0) {
+        a.head_base = full * 4;
+        e = launch_nh<PAGED, FUSED>(a, tbl, bits, tail, rows, 1, stream);
+    }
+    return e;
 }
 
 // outer-grouped blocks: the default ring depth only
@@ -1003,16 +1168,6 @@ hipError_t launch_outer_nh(const DecArgs &a, int bits, int nh, int64_t rows, int
     case 2: return launch_outer_bits<2>(a, nh, rows, chunks, stream);
     case 3: return launch_outer_bits<3>(a, nh, rows, chunks, stream);
     case 4: return launch_outer_bits<4>(a, nh, rows, chunks, stream);
-    default: return hipErrorInvalidValue;
-    }
-}
-
-hipError_t launch_nh(const DecArgs &a, int bits, int nh, int64_t rows, int chunks, hipStream_t stream)
-{
-    switch (bits) {
-    case 2: return launch_bits<2>(a, nh, rows, chunks, stream);
-    case 3: return launch_bits<3>(a, nh, rows, chunks, stream);
-    case 4: return launch_bits<4>(a, nh, rows, chunks, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1050,26 +1205,24 @@ hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream)
     return e;
 }
 
-hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream)
+static DecArgs paged_args(const DecodeParams &p)
 {
     DecArgs a = make_dec_args(p);
     a.row_stride = 0;
     a.row_bytes = 0;
     a.n_packed = 0;     // per sequence, from the state
     a.n_res = 0;
-    const int64_t rows = (int64_t)p.B * p.Hkv;
-    const int full = a.gq / 4, tail = a.gq % 4;
-    hipError_t e = hipSuccess;
-    if (full > 0) {
-        a.head_base = 0;
-        e = launch_paged_nh(a, p.tbl, p.bits, 4, rows, full, stream);
-        if (e != hipSuccess) return e;
-    }
-    if (tail > 0) {
-        a.head_base = full * 4;
-        e = launch_paged_nh(a, p.tbl, p.bits, tail, rows, 1, stream);
-    }
-    return e;
+    return a;
+}
+
+hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream)
+{
+    return launch_chunks<true, false>(paged_args(p), p.tbl, p.bits, (int64_t)p.B * p.Hkv, stream);
+}
+
+hipError_t launch_decode_paged_fused(const DecodeParams &p, hipStream_t stream)
+{
+    return launch_chunks<true, true>(paged_args(p), p.tbl, p.bits, (int64_t)p.B * p.Hkv, stream);
 }
 
 hipError_t launch_decode_outer(const DecodeParams &p, hipStream_t stream)
@@ -1092,20 +1245,14 @@ hipError_t launch_decode_outer(const DecodeParams &p, hipStream_t stream)
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream)
 {
-    DecArgs a = make_dec_args(p);
-    const int64_t rows = (int64_t)p.B * p.Hkv;
-    const int full = a.gq / 4, tail = a.gq % 4;
-    hipError_t e = hipSuccess;
-    if (full > 0) {
-        a.head_base = 0;
-        e = launch_nh(a, p.bits, 4, rows, full, stream);
-        if (e != hipSuccess) return e;
-    }
-    if (tail > 0) {
-        a.head_base = full * 4;
-        e = launch_nh(a, p.bits, tail, rows, 1, stream);
-    }
-    return e;
+    return launch_chunks<false, false>(make_dec_args(p), nullptr, p.bits, (int64_t)p.B * p.Hkv,
+                                       stream);
+}
+
+hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream)
+{
+    return launch_chunks<false, true>(make_dec_args(p), nullptr, p.bits, (int64_t)p.B * p.Hkv,
+                                      stream);
 }
 
 }  // namespace kvq

@@ -87,12 +87,71 @@ kvq_status kvq_quantize_pack_outer(const kvq_format *fmt, const void *src_fp16, 
 
 namespace {
 
+// Where a decode call leaves its result: the split partials (part_o, part_lse), or, for the
+// fused calls, the merged output (out, out_dtype) with the workspace of the in-launch merge.
+struct DecodeSink {
+    float *part_o = nullptr, *part_lse = nullptr;
+    void *out = nullptr;
+    int32_t out_dtype = 0;
+    void *ws = nullptr;
+    int64_t ws_bytes = 0;
+    bool fused = false;
+};
+
+DecodeSink partials(float *part_o, float *part_lse)
+{
+    DecodeSink k;
+    k.part_o = part_o;
+    k.part_lse = part_lse;
+    return k;
+}
+
+DecodeSink merged(void *out, int32_t out_dtype, void *ws, int64_t ws_bytes)
+{
+    DecodeSink k;
+    k.out = out;
+    k.out_dtype = out_dtype;
+    k.ws = ws;
+    k.ws_bytes = ws_bytes;
+    k.fused = true;
+    return k;
+}
+
+// checks of the result arguments shared by every decode call
+kvq_status check_sink(const DecodeSink &k, int32_t B, int32_t Hq, int32_t Hkv, int32_t S)
+{
+    if (!k.fused) {
+        if (!k.part_o || !k.part_lse) return KVQ_ERR_NULL;
+        if (!aligned64(k.part_o) || !aligned64(k.part_lse)) return KVQ_ERR_ALIGN;
+        return KVQ_OK;
+    }
+    if (!k.out) return KVQ_ERR_NULL;
+    if (k.out_dtype != KVQ_OUT_F32 && k.out_dtype != KVQ_OUT_F16) return KVQ_ERR_UNSUPPORTED;
+    if (!aligned64(k.out)) return KVQ_ERR_ALIGN;
+    const int64_t need = kvq::fused_workspace_bytes(B, Hq, Hkv, S);
+    if (need > 0) {
+        if (!k.ws) return KVQ_ERR_NULL;
+        if ((reinterpret_cast<uintptr_t>(k.ws) & 255u) != 0) return KVQ_ERR_ALIGN;
+        if (k.ws_bytes < need) return KVQ_ERR_SHAPE;
+    }
+    return KVQ_OK;
+}
+
+void fill_sink(kvq::DecodeParams &p, const DecodeSink &k)
+{
+    p.part_o = k.part_o;
+    p.part_lse = k.part_lse;
+    p.out = k.out;
+    p.out_f16 = k.out_dtype == KVQ_OUT_F16;
+    p.ws = k.ws;
+}
+
 kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq,
                          int32_t Hkv, const void *k_packed, const void *v_packed,
                          int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
                          const void *k_res_fp16, const void *v_res_fp16, int32_t res_capacity,
-                         int32_t n_res, float sm_scale, int32_t num_splits, float *part_o,
-                         float *part_lse, hipStream_t stream, int kind,
+                         int32_t n_res, float sm_scale, int32_t num_splits,
+                         const DecodeSink &sink, hipStream_t stream, int kind,
                          const float *qnorm = nullptr, const void *k_new = nullptr,
                          const void *v_new = nullptr)
 {
@@ -100,7 +159,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     if (kind == 2 && fmt && fmt->hybrid) return KVQ_ERR_UNSUPPORTED;
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
-    if (!q_fp16 || !part_o || !part_lse) return KVQ_ERR_NULL;
+    if (!q_fp16) return KVQ_ERR_NULL;
     if (n_packed_tokens > 0 && (!k_packed || !v_packed)) return KVQ_ERR_NULL;
     if (n_res > 0 && (!k_res_fp16 || !v_res_fp16)) return KVQ_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return KVQ_ERR_SHAPE;
@@ -112,6 +171,8 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
     if ((int64_t)B * Hq * fmt->head_dim * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
     if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
+    st = check_sink(sink, B, Hq, Hkv, num_splits);
+    if (st != KVQ_OK) return st;
     const int64_t bb = kvq_block_bytes(fmt);
     if (n_packed_tokens > 0) {
         if (packed_row_stride_bytes % 64 != 0) return KVQ_ERR_ALIGN;
@@ -120,7 +181,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
         if (!aligned64(k_packed) || !aligned64(v_packed)) return KVQ_ERR_ALIGN;
     }
     if (n_res > 0 && (!aligned64(k_res_fp16) || !aligned64(v_res_fp16))) return KVQ_ERR_ALIGN;
-    if (!aligned64(q_fp16) || !aligned64(part_o) || !aligned64(part_lse)) return KVQ_ERR_ALIGN;
+    if (!aligned64(q_fp16)) return KVQ_ERR_ALIGN;
     kvq::DecodeParams p{};
     p.q = static_cast<const uint16_t *>(q_fp16);
     p.B = B;
@@ -136,14 +197,14 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.n_res = n_res;
     p.sm_scale = sm_scale;
     p.num_splits = num_splits;
-    p.part_o = part_o;
-    p.part_lse = part_lse;
+    fill_sink(p, sink);
     p.bits = fmt->bits;
     p.block_bytes = (int32_t)bb;
     p.sz_off = (int32_t)kvq_sz_offset(fmt);
     p.qnorm = qnorm;
     p.knew = static_cast<const uint16_t *>(k_new);
     p.vnew = static_cast<const uint16_t *>(v_new);
+    if (sink.fused) return launched(kvq::launch_decode_fused(p, stream));
     if (kind == 2) return launched(kvq::launch_decode_outer(p, stream));
     return launched(kind == 1 ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
 }
@@ -162,7 +223,7 @@ kvq_status kvq_decode_attention(const kvq_format *fmt, const void *q_fp16, int32
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, 0);
+                         num_splits, partials(part_o, part_lse), stream, 0);
 }
 
 kvq_status kvq_decode_attention_append(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -179,7 +240,7 @@ kvq_status kvq_decode_attention_append(const kvq_format *fmt, const void *q_fp16
     if (!aligned64(k_new_fp16) || !aligned64(v_new_fp16)) return KVQ_ERR_ALIGN;
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, 0, nullptr, k_new_fp16,
+                         num_splits, partials(part_o, part_lse), stream, 0, nullptr, k_new_fp16,
                          v_new_fp16);
 }
 
@@ -196,7 +257,37 @@ kvq_status kvq_decode_attention_knorm(const kvq_format *fmt, const void *q_fp16,
     if (!aligned64(key_norm)) return KVQ_ERR_ALIGN;
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, 0, key_norm);
+                         num_splits, partials(part_o, part_lse), stream, 0, key_norm);
+}
+
+kvq_status kvq_decode_attention_fused(const kvq_format *fmt, const void *q_fp16,
+                                      const float *key_norm, int32_t B, int32_t Hq, int32_t Hkv,
+                                      const void *k_packed, const void *v_packed,
+                                      int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
+                                      void *k_res_fp16, void *v_res_fp16, int32_t res_capacity,
+                                      int32_t n_res, const void *k_new_fp16,
+                                      const void *v_new_fp16, float sm_scale, int32_t num_splits,
+                                      void *workspace, int64_t workspace_bytes, void *out,
+                                      int32_t out_dtype, hipStream_t stream)
+{
+    if ((k_new_fp16 == nullptr) != (v_new_fp16 == nullptr)) return KVQ_ERR_NULL;
+    if (k_new_fp16) {
+        if (!k_res_fp16 || !v_res_fp16) return KVQ_ERR_NULL;
+        if (n_res < 1) return KVQ_ERR_SHAPE;
+        if (!aligned64(k_new_fp16) || !aligned64(v_new_fp16)) return KVQ_ERR_ALIGN;
+    }
+    if (key_norm && !aligned64(key_norm)) return KVQ_ERR_ALIGN;
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, merged(out, out_dtype, workspace, workspace_bytes), stream,
+                         0, key_norm, k_new_fp16, v_new_fp16);
+}
+
+int64_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t num_splits)
+{
+    if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || num_splits < 1 || num_splits > 1024)
+        return -1;
+    return kvq::fused_workspace_bytes(B, Hq, Hkv, num_splits);
 }
 
 kvq_status kvq_decode_attention_outer(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -209,7 +300,7 @@ kvq_status kvq_decode_attention_outer(const kvq_format *fmt, const void *q_fp16,
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, 2);
+                         num_splits, partials(part_o, part_lse), stream, 2);
 }
 
 kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, int32_t B,
@@ -222,7 +313,7 @@ kvq_status kvq_decode_attention_valu(const kvq_format *fmt, const void *q_fp16, 
 {
     return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
-                         num_splits, part_o, part_lse, stream, 1);
+                         num_splits, partials(part_o, part_lse), stream, 1);
 }
 
 kvq_status kvq_decode_attention_fp16(const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv,
@@ -380,20 +471,22 @@ kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void
         reinterpret_cast<int32_t *>(state), B, Hkv, stream));
 }
 
-kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16, int32_t B,
-                                      int32_t Hq, int32_t Hkv, const void *k_pool,
-                                      const void *v_pool, int64_t pool_blocks,
-                                      int64_t block_stride_bytes, int64_t head_stride_bytes,
-                                      const int32_t *block_table, int32_t max_blocks,
-                                      const kvq_seq_state *state, const void *k_res_fp16,
-                                      const void *v_res_fp16, int32_t res_capacity,
-                                      const float *key_norm, float sm_scale, int32_t num_splits,
-                                      float *part_o, float *part_lse, hipStream_t stream)
+}  // extern "C"
+
+namespace {
+
+kvq_status paged_common(const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq,
+                        int32_t Hkv, const void *k_pool, const void *v_pool, int64_t pool_blocks,
+                        int64_t block_stride_bytes, int64_t head_stride_bytes,
+                        const int32_t *block_table, int32_t max_blocks,
+                        const kvq_seq_state *state, const void *k_res_fp16,
+                        const void *v_res_fp16, int32_t res_capacity, const float *key_norm,
+                        float sm_scale, int32_t num_splits, const DecodeSink &sink,
+                        hipStream_t stream)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
-    if (!q_fp16 || !k_pool || !v_pool || !state || !k_res_fp16 || !v_res_fp16 || !part_o ||
-        !part_lse)
+    if (!q_fp16 || !k_pool || !v_pool || !state || !k_res_fp16 || !v_res_fp16)
         return KVQ_ERR_NULL;
     if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || res_capacity < 1) return KVQ_ERR_SHAPE;
     if (num_splits < 1 || num_splits > 1024) return KVQ_ERR_SHAPE;
@@ -401,9 +494,10 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
     if ((int64_t)B * Hkv > 0x7fffffffLL) return KVQ_ERR_SHAPE;
     if (Hq / Hkv > 16) return KVQ_ERR_UNSUPPORTED;
     if ((int64_t)B * Hq * fmt->head_dim * 2 > 0x7fffffffLL) return KVQ_ERR_UNSUPPORTED;
+    st = check_sink(sink, B, Hq, Hkv, num_splits);
+    if (st != KVQ_OK) return st;
     if (!aligned64(q_fp16) || !aligned64(k_pool) || !aligned64(v_pool) || !aligned64(state) ||
-        !aligned64(k_res_fp16) || !aligned64(v_res_fp16) || !aligned64(part_o) ||
-        !aligned64(part_lse) || (key_norm && !aligned64(key_norm)))
+        !aligned64(k_res_fp16) || !aligned64(v_res_fp16) || (key_norm && !aligned64(key_norm)))
         return KVQ_ERR_ALIGN;
     kvq::PagedPool pp{};
     st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
@@ -422,8 +516,7 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
     p.res_cap = res_capacity;
     p.sm_scale = sm_scale;
     p.num_splits = num_splits;
-    p.part_o = part_o;
-    p.part_lse = part_lse;
+    fill_sink(p, sink);
     p.bits = fmt->bits;
     p.block_bytes = pp.block_bytes;
     p.sz_off = pp.sz_off;
@@ -433,7 +526,46 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
     p.block_stride = block_stride_bytes;
     p.head_stride = head_stride_bytes;
     p.state = reinterpret_cast<const int32_t *>(state);
-    return launched(kvq::launch_decode_paged(p, stream));
+    return launched(sink.fused ? kvq::launch_decode_paged_fused(p, stream)
+                               : kvq::launch_decode_paged(p, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                      int32_t Hq, int32_t Hkv, const void *k_pool,
+                                      const void *v_pool, int64_t pool_blocks,
+                                      int64_t block_stride_bytes, int64_t head_stride_bytes,
+                                      const int32_t *block_table, int32_t max_blocks,
+                                      const kvq_seq_state *state, const void *k_res_fp16,
+                                      const void *v_res_fp16, int32_t res_capacity,
+                                      const float *key_norm, float sm_scale, int32_t num_splits,
+                                      float *part_o, float *part_lse, hipStream_t stream)
+{
+    return paged_common(fmt, q_fp16, B, Hq, Hkv, k_pool, v_pool, pool_blocks, block_stride_bytes,
+                        head_stride_bytes, block_table, max_blocks, state, k_res_fp16, v_res_fp16,
+                        res_capacity, key_norm, sm_scale, num_splits, partials(part_o, part_lse),
+                        stream);
+}
+
+kvq_status kvq_decode_attention_paged_fused(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                            int32_t Hq, int32_t Hkv, const void *k_pool,
+                                            const void *v_pool, int64_t pool_blocks,
+                                            int64_t block_stride_bytes,
+                                            int64_t head_stride_bytes, const int32_t *block_table,
+                                            int32_t max_blocks, const kvq_seq_state *state,
+                                            const void *k_res_fp16, const void *v_res_fp16,
+                                            int32_t res_capacity, const float *key_norm,
+                                            float sm_scale, int32_t num_splits, void *workspace,
+                                            int64_t workspace_bytes, void *out, int32_t out_dtype,
+                                            hipStream_t stream)
+{
+    return paged_common(fmt, q_fp16, B, Hq, Hkv, k_pool, v_pool, pool_blocks, block_stride_bytes,
+                        head_stride_bytes, block_table, max_blocks, state, k_res_fp16, v_res_fp16,
+                        res_capacity, key_norm, sm_scale, num_splits,
+                        merged(out, out_dtype, workspace, workspace_bytes), stream);
 }
 
 kvq_status kvq_key_norm(const void *k_fp16, int64_t n_rows, int32_t n_tokens,

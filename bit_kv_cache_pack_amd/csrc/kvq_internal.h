@@ -34,9 +34,30 @@ struct DecodeParams {
     int32_t max_blocks;
     int64_t pool_blocks, block_stride, head_stride;
     const int32_t *state;
+    // split merge inside the launch (the fused calls): output and workspace
+    void *out;
+    int32_t out_f16;
+    void *ws;
 };
 
+// Workspace of the fused split merge: per group (a row's chunk of up to 4 query heads) one
+// 2080-byte slot per node below the root of the fan-in-8 split tree (a record, plus the
+// counter of the node's parent in the padding of its first child's slot).
+inline int32_t fused_records(int32_t S)
+{
+    int32_t r = 0;
+    for (int32_t n = S; n > 1; n = (n + 7) / 8) r += n;
+    return r;
+}
+inline int64_t fused_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S)
+{
+    const int64_t groups = (int64_t)B * Hkv * ((Hq / Hkv + 3) / 4);
+    return groups * (int64_t)fused_records(S) * 2080;
+}
+
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream);
+hipError_t launch_decode_paged_fused(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_outer(const DecodeParams &p, hipStream_t stream);

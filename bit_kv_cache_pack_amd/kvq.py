@@ -26,7 +26,10 @@ EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_k
             "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
             "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale", "kvq_pack_tokens_paged",
             "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
-            "kvq_decode_attention_outer", "kvq_decode_attention_append")
+            "kvq_decode_attention_outer", "kvq_decode_attention_append",
+            "kvq_decode_attention_fused", "kvq_decode_attention_paged_fused")
+# exported calls that return a size rather than a status
+EXPORTED_SIZE = ("kvq_decode_workspace_bytes",)
 
 
 class KVQError(RuntimeError):
@@ -125,6 +128,14 @@ def lib():
         L.kvq_decode_attention_paged.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64, i64,
                                                  vp, i32, vp, vp, vp, i32, vp, f32, i32, vp, vp,
                                                  vp]
+        L.kvq_decode_attention_fused.argtypes = [fp, vp, vp, i32, i32, i32, vp, vp, i64, i32,
+                                                 vp, vp, i32, i32, vp, vp, f32, i32, vp, i64,
+                                                 vp, i32, vp]
+        L.kvq_decode_attention_paged_fused.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64,
+                                                       i64, vp, i32, vp, vp, vp, i32, vp, f32,
+                                                       i32, vp, i64, vp, i32, vp]
+        L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+        L.kvq_decode_workspace_bytes.restype = i64
         for n in EXPORTED:
             getattr(L, n).restype = C.c_int
         _lib = L
@@ -322,6 +333,49 @@ def kvq_decode_attention_paged(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k
                                           num_splits, _ptr(part_o), _ptr(part_lse),
                                           _stream(stream, q_fp16))
     _check("kvq_decode_attention_paged", st)
+
+
+def kvq_decode_workspace_bytes(B: int, Hq: int, Hkv: int, num_splits: int) -> int:
+    n = lib().kvq_decode_workspace_bytes(B, Hq, Hkv, num_splits)
+    if n < 0:
+        raise KVQError("kvq_decode_workspace_bytes", KVQ_ERR_SHAPE)
+    return int(n)
+
+
+def kvq_decode_attention_fused(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
+                               v_packed, packed_row_stride_bytes: int, n_packed_tokens: int,
+                               k_res_fp16, v_res_fp16, res_capacity: int, n_res: int,
+                               sm_scale: float, num_splits: int, workspace, workspace_bytes: int,
+                               out, out_dtype: int = KVQ_OUT_F32, key_norm=None, k_new_fp16=None,
+                               v_new_fp16=None, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_fused(C.byref(f), _ptr(q_fp16), _ptr(key_norm), B, Hq, Hkv,
+                                          _ptr(k_packed), _ptr(v_packed),
+                                          packed_row_stride_bytes, n_packed_tokens,
+                                          _ptr(k_res_fp16), _ptr(v_res_fp16), res_capacity,
+                                          n_res, _ptr(k_new_fp16), _ptr(v_new_fp16),
+                                          float(sm_scale), num_splits, _ptr(workspace),
+                                          workspace_bytes, _ptr(out), out_dtype,
+                                          _stream(stream, q_fp16))
+    _check("kvq_decode_attention_fused", st)
+
+
+def kvq_decode_attention_paged_fused(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_pool,
+                                     v_pool, pool_blocks: int, block_stride_bytes: int,
+                                     head_stride_bytes: int, block_table, max_blocks: int, state,
+                                     k_res_fp16, v_res_fp16, res_capacity: int, sm_scale: float,
+                                     num_splits: int, workspace, workspace_bytes: int, out,
+                                     out_dtype: int = KVQ_OUT_F32, key_norm=None, stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_paged_fused(C.byref(f), _ptr(q_fp16), B, Hq, Hkv,
+                                                _ptr(k_pool), _ptr(v_pool), pool_blocks,
+                                                block_stride_bytes, head_stride_bytes,
+                                                _ptr(block_table), max_blocks, _ptr(state),
+                                                _ptr(k_res_fp16), _ptr(v_res_fp16), res_capacity,
+                                                _ptr(key_norm), float(sm_scale), num_splits,
+                                                _ptr(workspace), workspace_bytes, _ptr(out),
+                                                out_dtype, _stream(stream, q_fp16))
+    _check("kvq_decode_attention_paged_fused", st)
 
 
 def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:

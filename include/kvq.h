@@ -359,13 +359,64 @@ kvq_status kvq_decode_attention_fp16(const void *q_fp16, int32_t B, int32_t Hq, 
  * kvq_combine -- merge the split partials into the attention output (the log-sum-exp
  * merge of split-K flash-decoding, the FP16 baseline named in [BitDecoding] sec. 4.2):
  *   M = max_s lse_s, w_s = e^(lse_s - M), out = sum_s w_s o_s / sum_s w_s.
- * Splits with lse = -inf weigh 0. Every (b, h) must have at least one non-empty split.
+ * Splits with lse = -inf weigh 0; a (b, h) whose splits are all empty gets 0.
  *   out             [B][Hq][head_dim], fp32 (KVQ_OUT_F32) or fp16 rounded to nearest even
  *                   from the fp32 result (KVQ_OUT_F16)
  */
 kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
                        int32_t head_dim, int32_t num_splits, void *out, int32_t out_dtype,
                        hipStream_t stream);
+
+/*
+ * kvq_decode_attention_fused -- one whole decode step in one launch: the split-K partials
+ * of kvq_decode_attention (optionally with kvq_decode_attention_knorm's query scaling and
+ * kvq_decode_attention_append's new token) merged into the output inside the same launch,
+ * by the log-sum-exp rule of kvq_combine ([BitDecoding] sec. 2.2-2.3 for the decode,
+ * sec. 4.2 for the split-K merge). The splits of each (batch, kv-head, chunk of up to 4
+ * query heads) merge in a tree of fan-in 8: every split stores its partial in the
+ * workspace and counts itself in its parent's counter, and the last of a parent's children
+ * merges them; no workgroup waits for another.
+ *   key_norm        NULL, or fp32 [B*Hkv][128] key-channel factors (as kvq_decode_attention_knorm)
+ *   k_new_fp16, v_new_fp16  NULL (both), or the new token [B][Hkv][head_dim] that becomes
+ *                   window slot n_res - 1, as in kvq_decode_attention_append (the windows are
+ *                   then written and n_res >= 1)
+ *   workspace       device memory of at least kvq_decode_workspace_bytes(B, Hq, Hkv,
+ *                   num_splits) bytes, 256-byte aligned; may be NULL when that size is 0
+ *                   (num_splits == 1). It must be zeroed before its first use; every call
+ *                   leaves its counters at zero again (each is reset by the workgroup that
+ *                   completes it; the records need no clearing), so one zeroed workspace
+ *                   serves any sequence of calls of any shape that fits. Calls that share a
+ *                   workspace and may overlap (other streams) race; give them separate
+ *                   workspaces. A launch that does not complete (a device fault) leaves it
+ *                   undefined: zero it again.
+ *   out             [B][Hq][head_dim], fp32 (KVQ_OUT_F32) or fp16 (KVQ_OUT_F16: the
+ *                   round-to-nearest-even of the fp32 value the kernel computed)
+ *   other arguments, the split rule, validation and limits: as kvq_decode_attention.
+ *   KVQ_ERR_SHAPE if workspace_bytes is too small; a (b, h) that attends no token gets 0.
+ * The result equals kvq_decode_attention + kvq_combine up to floating-point rounding (the
+ * merge order differs).
+ */
+kvq_status kvq_decode_attention_fused(const kvq_format *fmt, const void *q_fp16,
+                                      const float *key_norm, int32_t B, int32_t Hq, int32_t Hkv,
+                                      const void *k_packed, const void *v_packed,
+                                      int64_t packed_row_stride_bytes, int32_t n_packed_tokens,
+                                      void *k_res_fp16, void *v_res_fp16, int32_t res_capacity,
+                                      int32_t n_res, const void *k_new_fp16,
+                                      const void *v_new_fp16, float sm_scale, int32_t num_splits,
+                                      void *workspace, int64_t workspace_bytes, void *out,
+                                      int32_t out_dtype, hipStream_t stream);
+
+/*
+ * kvq_decode_workspace_bytes -- bytes of workspace kvq_decode_attention_fused and
+ * kvq_decode_attention_paged_fused need for these sizes (0 when num_splits == 1; -1 for
+ * sizes those calls reject): per chunk of up to 4 query heads of every (batch, kv-head),
+ * one 2080-byte slot per node below the root of the fan-in-8 split tree (the node's
+ * partial: 4 x 128 fp32 outputs and 4 log-sum-exps; its padding word holds the counter of
+ * the parent whose first child it is). Every call lays its slots out from the start of the
+ * workspace on the same 2080-byte grid, which is why one zeroed workspace serves calls of
+ * any shape.
+ */
+int64_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t num_splits);
 
 /*
  * kvq_append_residual -- write one new fp16 token per (batch, kv-head) into residual slot
@@ -487,7 +538,7 @@ kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void
  * with num_splits S > 1 and n_res > 0 split S-1 holds the window and splits 0..S-2 share
  * the tiles, otherwise all S share them and split S-1 also takes the window; split s of
  * the Sp sharing splits gets tiles [s*NT/Sp, (s+1)*NT/Sp). Empty splits have lse = -inf
- * and o = 0; every sequence needs at least one token for kvq_combine to be defined.
+ * and o = 0; kvq_combine gives 0 for a sequence that attends no token.
  *   key_norm        NULL, or the fp32 [B*Hkv][128] key-channel factors of a cache whose keys
  *                   were normalized: q is then multiplied by them as in
  *                   kvq_decode_attention_knorm (64-byte aligned)
@@ -502,6 +553,24 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
                                       const void *v_res_fp16, int32_t res_capacity,
                                       const float *key_norm, float sm_scale, int32_t num_splits,
                                       float *part_o, float *part_lse, hipStream_t stream);
+
+/*
+ * kvq_decode_attention_paged_fused -- kvq_decode_attention_paged with the split merge in
+ * the same launch, as kvq_decode_attention_fused: the output [B][Hq][head_dim] (out_dtype
+ * as kvq_combine), the workspace as for kvq_decode_attention_fused. A sequence that attends
+ * no token gets 0. Other arguments, validation and limits: as kvq_decode_attention_paged.
+ */
+kvq_status kvq_decode_attention_paged_fused(const kvq_format *fmt, const void *q_fp16, int32_t B,
+                                            int32_t Hq, int32_t Hkv, const void *k_pool,
+                                            const void *v_pool, int64_t pool_blocks,
+                                            int64_t block_stride_bytes,
+                                            int64_t head_stride_bytes, const int32_t *block_table,
+                                            int32_t max_blocks, const kvq_seq_state *state,
+                                            const void *k_res_fp16, const void *v_res_fp16,
+                                            int32_t res_capacity, const float *key_norm,
+                                            float sm_scale, int32_t num_splits, void *workspace,
+                                            int64_t workspace_bytes, void *out, int32_t out_dtype,
+                                            hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -16,16 +16,18 @@ A = 1 << 20          # a fake, 64-byte aligned "device" address (never dereferen
 MIS = A + 2          # misaligned
 
 
-def _declared():
+def _declared(ret="kvq_status"):
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^kvq_status\s+(kvq_\w+)\s*\(", src, re.M)))
+    return sorted(set(re.findall(r"^" + ret + r"\s+(kvq_\w+)\s*\(", src, re.M)))
 
 
 def test_library_exports_every_declared_call():
     names = _declared()
     assert names == sorted(K.EXPORTED)
+    sizes = _declared("int64_t")
+    assert sizes == sorted(K.EXPORTED_SIZE)
     L = K.lib()
-    for n in names:
+    for n in names + sizes:
         assert hasattr(L, n), n
 
 
@@ -442,3 +444,77 @@ def test_split_rule_on_the_workloads():
     got = {n: K.suggest_splits(w.B, w.Hkv, w.L) for n, w in S.WORKLOADS.items()}
     assert got == {"tiny": 4, "llama8b_32k": 64, "batch8_2bit_hybrid": 12,
                    "long_128k_3bit": 64, "mha_b64_append": 1}
+
+
+# ---- the fused decode (split merge inside the launch) ------------------------------------
+
+def _ws_bytes(B, Hq, Hkv, S):
+    """The header's workspace size: per (batch, kv-head, chunk of <= 4 query heads) one
+    2080-byte slot per node below the root of the fan-in-8 split tree."""
+    slots = 0
+    n = S
+    while n > 1:
+        slots += n
+        n = (n + 7) // 8
+    return B * Hkv * ((Hq // Hkv + 3) // 4) * slots * 2080
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,S", [(1, 32, 8, 1), (1, 32, 8, 64), (8, 32, 8, 12),
+                                         (1, 8, 2, 9), (2, 40, 40, 3), (1, 10, 2, 1024),
+                                         (3, 48, 3, 513)])
+def test_decode_workspace_bytes(B, Hq, Hkv, S):
+    assert K.kvq_decode_workspace_bytes(B, Hq, Hkv, S) == _ws_bytes(B, Hq, Hkv, S)
+
+
+def test_decode_workspace_bytes_known_values():
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 1) == 0
+    # 8 rows x 1 chunk; S = 64: 64 + 8 slots
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 64) == 8 * 72 * 2080
+    for bad in [(0, 8, 2, 4), (1, 8, 3, 4), (1, 8, 2, 0), (1, 8, 2, 1025)]:
+        assert K.lib().kvq_decode_workspace_bytes(*bad) == -1
+
+
+W = 1 << 24          # a fake, 256-byte aligned workspace address
+
+
+def _fused(fmt=None, q=A, kn=None, B=1, Hq=8, Hkv=2, kp=A, vp=A, stride=10240, n_packed=128,
+           kr=A, vr=A, cap=128, n_res=4, knew=None, vnew=None, sm=0.088, S=4, ws=W,
+           wsb=1 << 20, out=A, od=K.KVQ_OUT_F32):
+    f = _fmt() if fmt is None else fmt
+    return K.lib().kvq_decode_attention_fused(C.byref(f), q, kn, B, Hq, Hkv, kp, vp, stride,
+                                              n_packed, kr, vr, cap, n_res, knew, vnew, sm, S, ws,
+                                              wsb, out, od, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(fmt=_fmt(bits=7)), K.KVQ_ERR_UNSUPPORTED),
+    (dict(q=None), K.KVQ_ERR_NULL),
+    (dict(out=None), K.KVQ_ERR_NULL),
+    (dict(ws=None), K.KVQ_ERR_NULL),
+    (dict(kp=None), K.KVQ_ERR_NULL),
+    (dict(knew=A), K.KVQ_ERR_NULL),                 # k_new without v_new
+    (dict(knew=A, vnew=A, kr=None), K.KVQ_ERR_NULL),
+    (dict(knew=A, vnew=A, n_res=0), K.KVQ_ERR_SHAPE),
+    (dict(knew=MIS, vnew=A), K.KVQ_ERR_ALIGN),
+    (dict(kn=MIS), K.KVQ_ERR_ALIGN),
+    (dict(od=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(out=MIS), K.KVQ_ERR_ALIGN),
+    (dict(ws=W + 64), K.KVQ_ERR_ALIGN),             # 64-byte but not 256-byte aligned
+    (dict(wsb=_ws_bytes(1, 8, 2, 4) - 1), K.KVQ_ERR_SHAPE),
+    (dict(Hq=6, Hkv=4), K.KVQ_ERR_SHAPE),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(S=1025), K.KVQ_ERR_SHAPE),
+    (dict(n_packed=0, n_res=0), K.KVQ_ERR_SHAPE),
+    (dict(sm=float("nan")), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(q=MIS), K.KVQ_ERR_ALIGN),
+])
+def test_decode_fused_rejects(kw, status):
+    assert _fused(**kw) == status
+
+
+def test_decode_fused_one_split_needs_no_workspace():
+    """With one split nothing is merged: a NULL workspace of size 0 passes validation (the
+    call then launches, so only the rejection of a bad out pointer is checked here)."""
+    assert _fused(S=1, ws=None, wsb=0, out=MIS) == K.KVQ_ERR_ALIGN
+    assert _fused(S=2, ws=None, wsb=0, out=A) == K.KVQ_ERR_NULL
