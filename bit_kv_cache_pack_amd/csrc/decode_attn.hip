@@ -38,10 +38,12 @@
 //    slice to reach the PV operand layout, and the V scales are read straight from the
 //    staged tile.
 #include "decode_common.h"
+#include "kvq.h"
 #include "kvq_internal.h"
 
 #include <math.h>
 
+#include <mutex>
 #include <type_traits>
 
 namespace kvq {
@@ -1253,6 +1255,65 @@ hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream)
 {
     return launch_chunks<false, true>(make_dec_args(p), nullptr, p.bits, (int64_t)p.B * p.Hkv,
                                       stream);
+}
+
+
+// ---------------------------------------------------------------------------------------
+// Scratch of the allocation-free fused decode (kvq_decode_attention_fused_noalloc): the
+// split records and counters live in this array instead of a caller workspace. Every GPU
+// the library runs on holds its own copy until the process ends, and every call on that
+// GPU shares it. In host code `scratch` only stands in for the symbol: the kernels get the
+// device address that hipGetSymbolAddress returns for the current device.
+// ---------------------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kScratchBytes = KVQ_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+__global__ __launch_bounds__(256) void scratch_clear_kernel(uint8_t *p, size_t n)
+{
+    const size_t n16 = n / 16;
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += (size_t)gridDim.x * 256)
+        reinterpret_cast<u32x4 *>(p)[i] = u32x4{0u, 0u, 0u, 0u};
+}
+
+// the array's address on the current device: looked up, and zeroed by a kernel on
+// `stream`, at the first call on that device
+hipError_t scratch_on_device(void **ptr, hipStream_t stream)
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static void *addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(scratch_clear_kernel, dim3(512), dim3(256), 0, stream,
+                           static_cast<uint8_t *>(p), kScratchBytes);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        addr[dev] = p;
+    }
+    *ptr = addr[dev];
+    return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_decode_fused_noalloc(DecodeParams p, hipStream_t stream)
+{
+    if (fused_workspace_bytes(p.B, p.Hq, p.Hkv, p.num_splits) > (int64_t)kScratchBytes)
+        return hipErrorInvalidValue;
+    void *ws = nullptr;
+    const hipError_t e = scratch_on_device(&ws, stream);
+    if (e != hipSuccess) return e;
+    p.ws = ws;
+    return launch_decode_fused(p, stream);
 }
 
 }  // namespace kvq

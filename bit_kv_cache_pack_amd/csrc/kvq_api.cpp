@@ -96,6 +96,7 @@ struct DecodeSink {
     void *ws = nullptr;
     int64_t ws_bytes = 0;
     bool fused = false;
+    bool noalloc = false;     // records in the library's scratch array (ws unused)
 };
 
 DecodeSink partials(float *part_o, float *part_lse)
@@ -129,6 +130,7 @@ kvq_status check_sink(const DecodeSink &k, int32_t B, int32_t Hq, int32_t Hkv, i
     if (k.out_dtype != KVQ_OUT_F32 && k.out_dtype != KVQ_OUT_F16) return KVQ_ERR_UNSUPPORTED;
     if (!aligned64(k.out)) return KVQ_ERR_ALIGN;
     const int64_t need = kvq::fused_workspace_bytes(B, Hq, Hkv, S);
+    if (k.noalloc) return need > KVQ_NOALLOC_SCRATCH_BYTES ? KVQ_ERR_TOO_LARGE : KVQ_OK;
     if (need > 0) {
         if (!k.ws) return KVQ_ERR_NULL;
         if ((reinterpret_cast<uintptr_t>(k.ws) & 255u) != 0) return KVQ_ERR_ALIGN;
@@ -204,6 +206,7 @@ kvq_status decode_common(const kvq_format *fmt, const void *q_fp16, int32_t B, i
     p.qnorm = qnorm;
     p.knew = static_cast<const uint16_t *>(k_new);
     p.vnew = static_cast<const uint16_t *>(v_new);
+    if (sink.noalloc) return launched(kvq::launch_decode_fused_noalloc(p, stream));
     if (sink.fused) return launched(kvq::launch_decode_fused(p, stream));
     if (kind == 2) return launched(kvq::launch_decode_outer(p, stream));
     return launched(kind == 1 ? kvq::launch_decode_valu(p, stream) : kvq::launch_decode(p, stream));
@@ -281,6 +284,32 @@ kvq_status kvq_decode_attention_fused(const kvq_format *fmt, const void *q_fp16,
                          n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
                          num_splits, merged(out, out_dtype, workspace, workspace_bytes), stream,
                          0, key_norm, k_new_fp16, v_new_fp16);
+}
+
+kvq_status kvq_decode_attention_fused_noalloc(const kvq_format *fmt, const void *q_fp16,
+                                              const float *key_norm, int32_t B, int32_t Hq,
+                                              int32_t Hkv, const void *k_packed,
+                                              const void *v_packed,
+                                              int64_t packed_row_stride_bytes,
+                                              int32_t n_packed_tokens, void *k_res_fp16,
+                                              void *v_res_fp16, int32_t res_capacity,
+                                              int32_t n_res, const void *k_new_fp16,
+                                              const void *v_new_fp16, float sm_scale,
+                                              int32_t num_splits, void *out, int32_t out_dtype,
+                                              hipStream_t stream)
+{
+    if ((k_new_fp16 == nullptr) != (v_new_fp16 == nullptr)) return KVQ_ERR_NULL;
+    if (k_new_fp16) {
+        if (!k_res_fp16 || !v_res_fp16) return KVQ_ERR_NULL;
+        if (n_res < 1) return KVQ_ERR_SHAPE;
+        if (!aligned64(k_new_fp16) || !aligned64(v_new_fp16)) return KVQ_ERR_ALIGN;
+    }
+    if (key_norm && !aligned64(key_norm)) return KVQ_ERR_ALIGN;
+    DecodeSink sink = merged(out, out_dtype, nullptr, 0);
+    sink.noalloc = true;
+    return decode_common(fmt, q_fp16, B, Hq, Hkv, k_packed, v_packed, packed_row_stride_bytes,
+                         n_packed_tokens, k_res_fp16, v_res_fp16, res_capacity, n_res, sm_scale,
+                         num_splits, sink, stream, 0, key_norm, k_new_fp16, v_new_fp16);
 }
 
 int64_t kvq_decode_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t num_splits)

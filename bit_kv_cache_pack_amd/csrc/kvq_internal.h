@@ -57,6 +57,8 @@ inline int64_t fused_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t
 
 hipError_t launch_decode(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_fused(const DecodeParams &p, hipStream_t stream);
+// the fused decode with its records in the library's per-device scratch array (p.ws unused)
+hipError_t launch_decode_fused_noalloc(DecodeParams p, hipStream_t stream);
 hipError_t launch_decode_paged_fused(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_valu(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_decode_paged(const DecodeParams &p, hipStream_t stream);

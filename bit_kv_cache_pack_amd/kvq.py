@@ -16,18 +16,22 @@ LIB_PATH = os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5
+KVQ_ERR_TOO_LARGE = -6
+KVQ_NOALLOC_SCRATCH_BYTES = 8 << 20
 KVQ_OUT_F32, KVQ_OUT_F16 = 0, 1
 KVQ_SCALE_DIVIDE, KVQ_SCALE_MULTIPLY = 0, 1
 _STATUS = {0: "ok", -1: "null pointer", -2: "bad shape or stride",
            -3: "unsupported format or shape", -4: "misaligned pointer or stride",
-           -5: "kernel launch failed"}
+           -5: "kernel launch failed",
+           -6: "sizes exceed the fixed scratch of the allocation-free call"}
 
 EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_knorm",
             "kvq_decode_attention_valu", "kvq_decode_attention_fp16", "kvq_combine",
             "kvq_append_residual", "kvq_key_norm", "kvq_channel_scale", "kvq_pack_tokens_paged",
             "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
             "kvq_decode_attention_outer", "kvq_decode_attention_append",
-            "kvq_decode_attention_fused", "kvq_decode_attention_paged_fused")
+            "kvq_decode_attention_fused", "kvq_decode_attention_paged_fused",
+            "kvq_decode_attention_fused_noalloc")
 # exported calls that return a size rather than a status
 EXPORTED_SIZE = ("kvq_decode_workspace_bytes",)
 
@@ -134,6 +138,9 @@ def lib():
         L.kvq_decode_attention_paged_fused.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64,
                                                        i64, vp, i32, vp, vp, vp, i32, vp, f32,
                                                        i32, vp, i64, vp, i32, vp]
+        L.kvq_decode_attention_fused_noalloc.argtypes = [fp, vp, vp, i32, i32, i32, vp, vp, i64,
+                                                         i32, vp, vp, i32, i32, vp, vp, f32, i32,
+                                                         vp, i32, vp]
         L.kvq_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
         L.kvq_decode_workspace_bytes.restype = i64
         for n in EXPORTED:
@@ -358,6 +365,24 @@ def kvq_decode_attention_fused(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k
                                           workspace_bytes, _ptr(out), out_dtype,
                                           _stream(stream, q_fp16))
     _check("kvq_decode_attention_fused", st)
+
+
+def kvq_decode_attention_fused_noalloc(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_packed,
+                                       v_packed, packed_row_stride_bytes: int,
+                                       n_packed_tokens: int, k_res_fp16, v_res_fp16,
+                                       res_capacity: int, n_res: int, sm_scale: float,
+                                       num_splits: int, out, out_dtype: int = KVQ_OUT_F32,
+                                       key_norm=None, k_new_fp16=None, v_new_fp16=None,
+                                       stream=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_fused_noalloc(C.byref(f), _ptr(q_fp16), _ptr(key_norm), B,
+                                                  Hq, Hkv, _ptr(k_packed), _ptr(v_packed),
+                                                  packed_row_stride_bytes, n_packed_tokens,
+                                                  _ptr(k_res_fp16), _ptr(v_res_fp16),
+                                                  res_capacity, n_res, _ptr(k_new_fp16),
+                                                  _ptr(v_new_fp16), float(sm_scale), num_splits,
+                                                  _ptr(out), out_dtype, _stream(stream, q_fp16))
+    _check("kvq_decode_attention_fused_noalloc", st)
 
 
 def kvq_decode_attention_paged_fused(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_pool,

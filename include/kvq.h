@@ -93,8 +93,12 @@ typedef enum {
     KVQ_ERR_SHAPE = -2,       /* sizes or strides out of range or inconsistent */
     KVQ_ERR_UNSUPPORTED = -3, /* valid request that this build does not implement */
     KVQ_ERR_ALIGN = -4,       /* pointer or stride not aligned as required */
-    KVQ_ERR_LAUNCH = -5       /* the HIP runtime rejected a launch */
+    KVQ_ERR_LAUNCH = -5,      /* the HIP runtime rejected a launch */
+    KVQ_ERR_TOO_LARGE = -6    /* the sizes need more scratch than the allocation-free call has */
 } kvq_status;
+
+/* Bytes of device scratch behind kvq_decode_attention_fused_noalloc (one array per GPU). */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8 << 20)
 
 typedef struct {
     int32_t bits;         /* 2, 3 or 4 */
@@ -183,6 +187,7 @@ static inline const char *kvq_status_string(kvq_status s)
     case KVQ_ERR_UNSUPPORTED: return "unsupported format or shape";
     case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
     case KVQ_ERR_LAUNCH: return "kernel launch failed";
+    case KVQ_ERR_TOO_LARGE: return "sizes exceed the fixed scratch of the allocation-free call";
     }
     return "unknown status";
 }
@@ -405,6 +410,34 @@ kvq_status kvq_decode_attention_fused(const kvq_format *fmt, const void *q_fp16,
                                       const void *v_new_fp16, float sm_scale, int32_t num_splits,
                                       void *workspace, int64_t workspace_bytes, void *out,
                                       int32_t out_dtype, hipStream_t stream);
+
+/*
+ * kvq_decode_attention_fused_noalloc -- kvq_decode_attention_fused without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation). The split records live in a
+ * device array of KVQ_NOALLOC_SCRATCH_BYTES bytes that the library holds on each GPU it
+ * runs on until the process ends; the call allocates nothing (no hipMalloc, no allocating
+ * library routine). The first call on a device (the current device) looks the array up and
+ * enqueues one kernel that zeroes it; every call leaves its counters at zero again.
+ *   Arguments, outputs, validation and limits: as kvq_decode_attention_fused without
+ *   workspace / workspace_bytes; KVQ_ERR_TOO_LARGE when kvq_decode_workspace_bytes(B, Hq,
+ *   Hkv, num_splits) exceeds KVQ_NOALLOC_SCRATCH_BYTES (e.g. 8 rows of 4 query heads take
+ *   1.2 MB at 64 splits; 1024 splits need 19.5 MB and are rejected).
+ *   Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (other
+ *   streams, other threads) race and give undefined results; serialize them, or use
+ *   kvq_decode_attention_fused with separate workspaces.
+ */
+kvq_status kvq_decode_attention_fused_noalloc(const kvq_format *fmt, const void *q_fp16,
+                                              const float *key_norm, int32_t B, int32_t Hq,
+                                              int32_t Hkv, const void *k_packed,
+                                              const void *v_packed,
+                                              int64_t packed_row_stride_bytes,
+                                              int32_t n_packed_tokens, void *k_res_fp16,
+                                              void *v_res_fp16, int32_t res_capacity,
+                                              int32_t n_res, const void *k_new_fp16,
+                                              const void *v_new_fp16, float sm_scale,
+                                              int32_t num_splits, void *out, int32_t out_dtype,
+                                              hipStream_t stream);
 
 /*
  * kvq_decode_workspace_bytes -- bytes of workspace kvq_decode_attention_fused and

@@ -518,3 +518,31 @@ def test_decode_fused_one_split_needs_no_workspace():
     call then launches, so only the rejection of a bad out pointer is checked here)."""
     assert _fused(S=1, ws=None, wsb=0, out=MIS) == K.KVQ_ERR_ALIGN
     assert _fused(S=2, ws=None, wsb=0, out=A) == K.KVQ_ERR_NULL
+
+
+def _noalloc(B=1, Hq=8, Hkv=2, n_packed=128, S=4, out=A, od=K.KVQ_OUT_F32, knew=None, vnew=None):
+    f = _fmt()
+    return K.lib().kvq_decode_attention_fused_noalloc(C.byref(f), A, None, B, Hq, Hkv, A, A,
+                                                      10240 * 256, n_packed, A, A, 128, 4, knew,
+                                                      vnew, 0.088, S, out, od, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), K.KVQ_ERR_NULL),
+    (dict(out=MIS), K.KVQ_ERR_ALIGN),
+    (dict(od=5), K.KVQ_ERR_UNSUPPORTED),
+    (dict(knew=A), K.KVQ_ERR_NULL),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    # 8 rows of 4 query heads at 1024 splits need 19.5 MB of records: more than the scratch
+    (dict(B=1, Hq=32, Hkv=8, n_packed=32768, S=1024), K.KVQ_ERR_TOO_LARGE),
+])
+def test_decode_fused_noalloc_rejects(kw, status):
+    assert _noalloc(**kw) == status
+
+
+def test_noalloc_scratch_limit_matches_header():
+    src = open(HEADER).read()
+    m = re.search(r"#define KVQ_NOALLOC_SCRATCH_BYTES \((\d+) << (\d+)\)", src)
+    assert m and int(m.group(1)) << int(m.group(2)) == K.KVQ_NOALLOC_SCRATCH_BYTES
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 1024) > K.KVQ_NOALLOC_SCRATCH_BYTES
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 64) <= K.KVQ_NOALLOC_SCRATCH_BYTES
