@@ -49,16 +49,14 @@
 namespace kvq {
 namespace {
 
-#ifndef KVQ_WAVES
-#define KVQ_WAVES 4
-#endif
 // LDS of one workgroup: a RING-slot ring of tiles per wave plus small staging arrays
 // (4-bit: ~49 KB with 2 slots, three workgroups per CU).
 // A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
-template <int TILE_BYTES, int RING, int W>
+template <int TILE_BYTES, int RING, int W, int QCOPIES = W>
 struct Smem {
     alignas(16) uint8_t ring[W][RING][TILE_BYTES];    // per-wave ring of staged tiles
-    alignas(16) uint16_t q[W][4][kHeadDim];            // per-wave copy of the chunk's q
+    alignas(16) uint16_t q[QCOPIES][4][kHeadDim];      // the chunk's q (one copy, or one per wave)
+    alignas(16) float qn[kHeadDim];                    // the row's key-channel norms (if any)
     alignas(16) float p[W][2][4][kTile];      // p of head h, token t of tiles 2j and 2j+1
     alignas(16) float ml[W][4][2];
     uint32_t flag;                            // last-arrival flag of the fused split merge
@@ -485,9 +483,12 @@ constexpr int kRecFloats = 520;
 constexpr int kCtrWord = 516;
 constexpr int kScDevice = 16;            // sc1: device-scope coherent load / store
 
+// Records are written and read by the workgroup's first 256 threads (4 heads x 64 threads x
+// 2 channels); the threads of an eight-wave workgroup beyond them only join the barriers.
 __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t rr, int rec, float v0, float v1,
                                           float lse2)
 {
+    if (threadIdx.x >= 256) return;
     const int h = threadIdx.x >> 6;
     const int d = (threadIdx.x & 63) * 2;
     const u32x2 v = {__float_as_uint(v0), __float_as_uint(v1)};
@@ -503,6 +504,10 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t rr, int rec, fl
 __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, int cnt, float &v0,
                                           float &v1, float &lse2)
 {
+    v0 = 0.f;
+    v1 = 0.f;
+    lse2 = -INFINITY;
+    if (threadIdx.x >= 256) return;
     const int h = threadIdx.x >> 6;
     const int d = (threadIdx.x & 63) * 2;
     u32x2 x[8];
@@ -604,11 +609,20 @@ __device__ __forceinline__ void merge_fused(SM &sm, const WaveState &st, int wav
     }
 }
 
-// The inner-grouped kernels are held to 168 VGPRs so that three workgroups (three waves
-// per SIMD) fit on a CU next to their 49 KB of LDS each; the outer-grouped comparison
-// kernel needs more registers and runs two.
+// Waves per SIMD that the LDS lets a CU hold (160 KB per CU, one Smem per workgroup of W
+// waves), at most three. The inner-grouped kernels ask the register allocator for that
+// occupancy (three waves per SIMD means at most 168 VGPRs); the outer-grouped comparison
+// kernel needs more registers and asks for one.
+template <int BITS, int RING, int W>
+constexpr int lds_waves_per_simd()
+{
+    constexpr int wgs = (160 * 1024) / (int)sizeof(Smem<TileGeom<BITS>::BYTES, RING, W, 1>);
+    constexpr int waves = wgs * W / 4;
+    return waves < 1 ? 1 : (waves > 3 ? 3 : waves);
+}
+
 template <int BITS, int NH, int RING, int W, bool PAGED, bool OUTER = false, bool FUSED = false>
-__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 1 : 3))) void decode_kernel(DecArgs a,
+__global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 1 : lds_waves_per_simd<BITS, RING, W>()))) void decode_kernel(DecArgs a,
                                                         const int32_t *__restrict__ tbl,
                                                         const int32_t *__restrict__ seq_state)
 {
@@ -616,7 +630,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
     static_assert(RING >= 2 && RING <= 8, "ring depth");
     static_assert(RING * G::BYTES >= 4 * kHeadDim * 4, "merge output must fit in a wave's ring");
     constexpr int kWaves = W;
-    __shared__ Smem<G::BYTES, RING, W> sm;
+    __shared__ Smem<G::BYTES, RING, W, 1> sm;
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform (SGPR)
     const int n = lane & 15;
@@ -684,35 +698,43 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         return kTile;
     };
 
-    // key-channel norms of this row's channels 8*(lane%16)..+7 when q is to be multiplied
-    // by them (loaded first, so they are older than every load waited for below)
-    float4_t qn0 = {}, qn1 = {};
-    if (a.qnorm) {
-        const float4_t *np = reinterpret_cast<const float4_t *>(a.qnorm + row * kHeadDim + 8 * n);
-        qn0 = np[0];
-        qn1 = np[1];
-    }
-
     // ---- q of the chunk's heads -> this wave's LDS copy (one 1 KB direct-to-LDS load,
     // issued before the tile requests so it is the oldest outstanding load) ----
     const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t *>(a.q), 0, a.q_bytes, kRsrcWord3);
-    dma(rq, reinterpret_cast<uint8_t *>(&sm.q[wave][0][0]),
-        (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
+    // (wave 0 stages q for the whole workgroup, and the row's 128 key-channel norms when q
+    // is to be multiplied by them; both straight into LDS, so that no load into registers is
+    // in flight next to the tile loads: the compiler would wait for all loads before
+    // reusing such a register)
+    if (wave == 0) {
+        dma(rq, reinterpret_cast<uint8_t *>(&sm.q[0][0][0]),
+            (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
+        if (a.qnorm && lane < 32) {
+            const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<float *>(a.qnorm + row * kHeadDim), 0, kHeadDim * 4, kRsrcWord3);
+            dma(rn, reinterpret_cast<uint8_t *>(&sm.qn[0]), lane * 16, 16);
+        }
+    }
 
     // ---- ask for this wave's first RING tiles ----
     const int my_lo = tlo + wave;
     const int nt_w = my_lo < thi ? (thi - my_lo + kWaves - 1) / kWaves : 0;
     uint8_t *ring = &sm.ring[wave][0][0];
+    // Only the first tile is asked for before the prologue (q, A operands), the rest right
+    // after it: the first tiles of all waves then reach the memory system ahead of the
+    // second ones (measured 0.2 us faster at 32K tokens than asking for both at once).
+    constexpr int kFirst = 1;
 #pragma unroll
-    for (int k = 0; k < RING; ++k)
+    for (int k = 0; k < kFirst; ++k)
         if (k < nt_w) issue(ring + k * G::BYTES, my_lo + k * kWaves);
-    wait_behind<BITS>(nt_w < RING ? nt_w : RING);     // q, issued before the tiles
-    if (a.qnorm) {
+    if (wave == 0) wait_behind<BITS>(nt_w < kFirst ? nt_w : kFirst);   // q, issued before the tiles
+    if (wave == 0 && a.qnorm) {
         // q' = fp16(q * norm) per channel: lane (r, n) rescales the 16 bytes it loaded
         // (head r of the chunk, channels 8n..8n+7) in place
-        u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.q[wave][r][8 * n]);
+        u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.q[0][r][8 * n]);
         const u32x4 w = *mine;
+        const float4_t qn0 = *reinterpret_cast<const float4_t *>(&sm.qn[8 * n]);
+        const float4_t qn1 = *reinterpret_cast<const float4_t *>(&sm.qn[8 * n + 4]);
         const float nv[8] = {qn0[0], qn0[1], qn0[2], qn0[3], qn1[0], qn1[1], qn1[2], qn1[3]};
         u32x4 o;
 #pragma unroll
@@ -724,8 +746,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
                    ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)y1) << 16);
         }
         *mine = o;
-        lds_fence();
     }
+    // q in LDS for every wave. A plain s_barrier: __syncthreads would also wait for this
+    // wave's tile loads (the compiler counts direct-to-LDS loads as LDS writes to release),
+    // while only wave 0's q (waited for above) and its q' stores must be complete here.
+    lds_fence();
+    __builtin_amdgcn_s_barrier();
 
     // ---- QK A operands and per-group sums sum_{c in g} q_h[c] ----
     // The query octets in the key operand's slot order; for the packed tiles slot pair p is
@@ -737,7 +763,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         const bool live = (gA == r) && (hA < NH);
 #pragma unroll
         for (int o = 0; o < 4; ++o) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hA][32 * r + 8 * o]);
+            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[0][hA][32 * r + 8 * o]);
             half8_t h = live ? perm_octet_f16(w) : half8_t{};
             if (weighted) {
 #pragma unroll
@@ -748,12 +774,15 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         }
     };
     build_aq(!OUTER);
+#pragma unroll
+    for (int k = kFirst; k < RING; ++k)
+        if (k < nt_w) issue(ring + k * G::BYTES, my_lo + k * kWaves);
     float qs[4];
     {
         // lane (hh, gg, qq) sums 8 channels; the quad sum is Qs[hh][gg]; lane (n, r) then
         // fetches Qs[r][g] from lane 16r + 4g
         const int hh = lane >> 4, gg = (lane >> 2) & 3, qq = lane & 3;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sm.q[wave][hh][gg * 32 + qq * 8]);
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sm.q[0][hh][gg * 32 + qq * 8]);
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -779,7 +808,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
 #pragma unroll
     for (int c = 0; c < 8; ++c) st.dpv[c] = float4_t{0.f, 0.f, 0.f, 0.f};
     using PV = std::conditional_t<OUTER, PVInO, PVIn>;
-    const uint16_t *qw = &sm.q[wave][0][0];
+    const uint16_t *qw = &sm.q[0][0][0];
     // stage A / stage B of one packed tile, for the inner or the outer grouping
     auto stage_a = [&](const uint8_t *slot, float *pw, PV &pv, float &alpha, bool &resc, int nv) {
         if constexpr (OUTER) {
@@ -1092,37 +1121,70 @@ hipError_t launch_f16_nh(const DecArgs &a, int64_t rows, int chunks, hipStream_t
 // 2 slots at 32K tokens), because the first tiles arrive later and one wave per SIMD
 // computes its tiles more slowly.
 
-template <int BITS, int NH, int R, bool PAGED = false, bool FUSED = false>
+template <int BITS, int NH, int R, int W, bool PAGED = false, bool FUSED = false>
 hipError_t launch_r(const DecArgs &a, dim3 grid, hipStream_t stream, const int32_t *tbl = nullptr)
 {
-    constexpr int W = KVQ_WAVES;
     hipLaunchKernelGGL((decode_kernel<BITS, NH, R, W, PAGED, false, FUSED>), grid, dim3(64 * W), 0,
                        stream, a, tbl, a.state);
     return hipGetLastError();
 }
 
+// Compute units of the current device (looked up once per device).
+int cu_count()
+{
+    constexpr int kMaxDevices = 64;
+    static std::mutex mu;
+    static int cus[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cus[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            n < 1)
+            n = 256;
+        cus[dev] = n;
+    }
+    return cus[dev];
+}
+
+// Workgroup shape: when the grid has no more workgroups than the device has compute units,
+// each gets a CU of its own and eight waves (two per SIMD) share the split's tiles; with
+// more workgroups, four-wave workgroups let two or three of them share a CU.
 template <int BITS, bool PAGED, bool FUSED>
 hipError_t launch_bits(const DecArgs &a, const int32_t *tbl, int nh, int64_t rows, int chunks,
-                       hipStream_t stream)
+                       int64_t total_wgs, hipStream_t stream)
 {
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
+#ifndef KVQ_WIDE
+#define KVQ_WIDE 8
+#endif
+    if (total_wgs <= cu_count()) {
+        switch (nh) {
+        case 1: return launch_r<BITS, 1, KVQ_RING, KVQ_WIDE, PAGED, FUSED>(a, grid, stream, tbl);
+        case 2: return launch_r<BITS, 2, KVQ_RING, KVQ_WIDE, PAGED, FUSED>(a, grid, stream, tbl);
+        case 3: return launch_r<BITS, 3, KVQ_RING, KVQ_WIDE, PAGED, FUSED>(a, grid, stream, tbl);
+        case 4: return launch_r<BITS, 4, KVQ_RING, KVQ_WIDE, PAGED, FUSED>(a, grid, stream, tbl);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (nh) {
-    case 1: return launch_r<BITS, 1, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
-    case 2: return launch_r<BITS, 2, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
-    case 3: return launch_r<BITS, 3, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
-    case 4: return launch_r<BITS, 4, KVQ_RING, PAGED, FUSED>(a, grid, stream, tbl);
+    case 1: return launch_r<BITS, 1, KVQ_RING, 4, PAGED, FUSED>(a, grid, stream, tbl);
+    case 2: return launch_r<BITS, 2, KVQ_RING, 4, PAGED, FUSED>(a, grid, stream, tbl);
+    case 3: return launch_r<BITS, 3, KVQ_RING, 4, PAGED, FUSED>(a, grid, stream, tbl);
+    case 4: return launch_r<BITS, 4, KVQ_RING, 4, PAGED, FUSED>(a, grid, stream, tbl);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <bool PAGED, bool FUSED>
 hipError_t launch_nh(const DecArgs &a, const int32_t *tbl, int bits, int nh, int64_t rows,
-                     int chunks, hipStream_t stream)
+                     int chunks, int64_t total_wgs, hipStream_t stream)
 {
     switch (bits) {
-    case 2: return launch_bits<2, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
-    case 3: return launch_bits<3, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
-    case 4: return launch_bits<4, PAGED, FUSED>(a, tbl, nh, rows, chunks, stream);
+    case 2: return launch_bits<2, PAGED, FUSED>(a, tbl, nh, rows, chunks, total_wgs, stream);
+    case 3: return launch_bits<3, PAGED, FUSED>(a, tbl, nh, rows, chunks, total_wgs, stream);
+    case 4: return launch_bits<4, PAGED, FUSED>(a, tbl, nh, rows, chunks, total_wgs, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -1133,15 +1195,16 @@ template <bool PAGED, bool FUSED>
 hipError_t launch_chunks(DecArgs a, const int32_t *tbl, int bits, int64_t rows, hipStream_t stream)
 {
     const int full = a.gq / 4, tail = a.gq % 4;
+    const int64_t total_wgs = rows * a.S * (full + (tail > 0));
     hipError_t e = hipSuccess;
     if (full > 0) {
         a.head_base = 0;
-        e = launch_nh<PAGED, FUSED>(a, tbl, bits, 4, rows, full, stream);
+        e = launch_nh<PAGED, FUSED>(a, tbl, bits, 4, rows, full, total_wgs, stream);
         if (e != hipSuccess) return e;
     }
     if (tail > 0) {
         a.head_base = full * 4;
-        e = launch_nh<PAGED, FUSED>(a, tbl, bits, tail, rows, 1, stream);
+        e = launch_nh<PAGED, FUSED>(a, tbl, bits, tail, rows, 1, total_wgs, stream);
     }
     return e;
 }
@@ -1151,7 +1214,7 @@ template <int BITS>
 hipError_t launch_outer_bits(const DecArgs &a, int nh, int64_t rows, int chunks,
                              hipStream_t stream)
 {
-    constexpr int W = KVQ_WAVES;
+    constexpr int W = 4;
     const dim3 grid((uint32_t)rows, (uint32_t)a.S, (uint32_t)chunks);
     switch (nh) {
     case 1: hipLaunchKernelGGL((decode_kernel<BITS, 1, KVQ_RING, W, false, true>), grid, dim3(64 * W), 0, stream, a, nullptr, nullptr); break;

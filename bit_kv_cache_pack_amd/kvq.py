@@ -407,10 +407,13 @@ def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
     """Same rule as the header's kvq_suggest_splits."""
     rows = B * Hkv
     tiles = n_tokens // 32
-    want = (3 * cu_count + rows - 1) // rows
-    if tiles < 64 * want:
-        want = (2 * cu_count + rows - 1) // rows
     cap = tiles // 8
+    if rows >= 1 and 2 * rows <= cu_count and tiles <= 128 * (cu_count // rows):
+        want = cu_count // rows
+    else:
+        want = (3 * cu_count + rows - 1) // rows
+        if tiles < 64 * want:
+            want = (2 * cu_count + rows - 1) // rows
     return int(max(1, min(256, min(want, cap))))
 
 

@@ -144,19 +144,28 @@ static inline int64_t kvq_block_bytes(const kvq_format *f)
 {
     return kvq_align64(kvq_flag_offset(f) + kvq_flag_bytes(f));
 }
-/* A split count for decode on `cu_count` CUs: enough splits that B*Hkv*S workgroups give
-   three workgroups per CU (the decode kernel's registers and LDS allow three) while each
-   split keeps at least 64 packed 32-token tiles, else two per CU (shorter splits pay the
-   per-workgroup start and merge too often: two measured best at 32K tokens x 8 kv-heads
-   and at 128K x 8, three at 32K x 64), and never fewer than 8 tiles per split. */
+/* A split count for decode on `cu_count` CUs. When the B*Hkv rows are few (at most half
+   as many as CUs) and the sequence short enough that cu_count/rows splits leave each of
+   them at most 128 packed 32-token tiles, one split per CU per row: the launch then has
+   at most one workgroup per CU and takes the 8-wave kernel, which holds a whole CU's LDS
+   (measured best at 32K and 128K tokens x 8 kv-heads, 32 splits). Otherwise enough
+   splits that B*Hkv*S workgroups give three 4-wave workgroups per CU while each split
+   keeps at least 64 tiles, else two per CU (shorter splits pay the per-workgroup start
+   and merge too often; three measured best at 32K x 64 rows). Never fewer than 8 tiles
+   per split, never more than 256 splits. */
 static inline int32_t kvq_suggest_splits(int32_t B, int32_t Hkv, int32_t n_tokens,
                                          int32_t cu_count)
 {
     int64_t rows = (int64_t)B * Hkv;
     int64_t tiles = n_tokens / 32;
-    int64_t want = (3LL * cu_count + rows - 1) / rows;
-    if (tiles < 64 * want) want = (2LL * cu_count + rows - 1) / rows;
     int64_t cap = tiles / 8;
+    int64_t want;
+    if (rows >= 1 && 2 * rows <= cu_count && tiles <= 128LL * (cu_count / rows)) {
+        want = cu_count / rows;
+    } else {
+        want = (3LL * cu_count + rows - 1) / rows;
+        if (tiles < 64 * want) want = (2LL * cu_count + rows - 1) / rows;
+    }
     int64_t s = want < cap ? want : cap;
     if (s < 1) s = 1;
     if (s > 256) s = 256;

@@ -439,11 +439,17 @@ def test_split_rules_match_the_header(tmp_path):
 
 
 def test_split_rule_on_the_workloads():
-    """Three workgroups per CU where splits stay long, two where they would get short."""
+    """One wide workgroup per CU for few rows, else three 4-wave workgroups per CU where
+    splits stay long and two where they would get short; the 8-tile floor for short
+    sequences."""
     import synth_inputs as S
     got = {n: K.suggest_splits(w.B, w.Hkv, w.L) for n, w in S.WORKLOADS.items()}
-    assert got == {"tiny": 4, "llama8b_32k": 64, "batch8_2bit_hybrid": 12,
-                   "long_128k_3bit": 64, "mha_b64_append": 1}
+    assert got == {"tiny": 4, "llama8b_32k": 32, "batch8_2bit_hybrid": 12,
+                   "long_128k_3bit": 32, "mha_b64_append": 1}
+    # the wide branch: 32 rows on 256 CUs, 8 splits of 128 tiles; one tile more per split
+    # leaves it for the per-CU rules (two per CU: 16 splits)
+    assert K.suggest_splits(4, 8, 32768) == 8
+    assert K.suggest_splits(4, 8, 32768 + 8 * 32) == 16
 
 
 # ---- the fused decode (split merge inside the launch) ------------------------------------
