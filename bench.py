@@ -12,7 +12,11 @@ reported next to the step: the flush (kvq_quantize_pack of the 128-token window 
 row), the one-token append, the key-channel normalization passes over the prefill keys and
 the decode step with normalized queries, the FP16 flash-decoding baseline, the same step
 over outer-dimension (KIVI-style) groups, a serving-shaped paged batch, a plain device copy
-as a bandwidth reference, and the CPU oracle on a bounded sample of the same workload.
+and a plain streaming read of the step's bytes (same rotation) as bandwidth references, the
+CPU oracle on a bounded sample of the same workload (all host threads, and one thread), and,
+under "per_config", the step and decode figures of the other workloads (with the share of
+symmetric-mode groups for the hybrid cache, and the flush and amortized serving step where
+the window is full).
 
 Prints one JSON line.
 """
@@ -51,6 +55,10 @@ def parse():
     ap.add_argument("--paged-workload", default="paged_ragged_b16")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="skip the other workloads' step / decode figures")
+    ap.add_argument("--per-config-steps", type=int, default=200)
+    ap.add_argument("--cpu-single-seconds", type=float, default=3.0)
     return ap.parse_args()
 
 
@@ -76,7 +84,7 @@ def recorded_traffic(workload: str):
     return float(t.group(1))
 
 
-def cpu_baseline(wl, x, seconds: float):
+def cpu_baseline(wl, x, seconds: float, single_seconds: float):
     """The CPU oracle (fp64 dequant + attention), as it stands, on the host cores."""
     import numpy as np
     from oracle import oracle as O
@@ -87,19 +95,174 @@ def cpu_baseline(wl, x, seconds: float):
     vp = O.quantize_pack(fmt, np.ascontiguousarray(vps.reshape(rows, wl.n_packed, 128)))
     kr, vr = x.residual()
     threads = O.default_threads()
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        O.attention(fmt, x.q, wl.Hkv, kp, vp, wl.n_packed, kr, vr, wl.n_res, n_threads=threads)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
+
+    def run(n_threads, budget):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            O.attention(fmt, x.q, wl.Hkv, kp, vp, wl.n_packed, kr, vr, wl.n_res,
+                        n_threads=n_threads)
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= budget:
+                return reps, el
+
+    reps, el = run(threads, seconds)
     step_s = el / reps
+    reps1, el1 = run(1, single_seconds)
     return {"value": round(wl.step_bytes() / step_s / 1e9, 4), "unit": "GB/s",
             "cores": threads, "kind": "oracle",
             "ms_per_step": round(step_s * 1e3, 3),
+            "single_thread_ms_per_step": round(el1 / reps1 * 1e3, 3),
+            "single_thread_GB_per_s": round(wl.step_bytes() / (el1 / reps1) / 1e9, 4),
+            "cpu_model": cpu_model(),
             "sample": f"{reps} full decode steps of {wl.name} (all {wl.B * wl.Hq} heads, "
-                      f"{wl.L} tokens; dequantize + fp64 softmax attention), {el:.1f} s"}
+                      f"{wl.L} tokens; dequantize + fp64 softmax attention) on {threads} "
+                      f"threads, {el:.1f} s; {reps1} steps on one thread, {el1:.1f} s"}
+
+
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def flag_sym_ratio(fmt, caches_kv, rows, nb):
+    """Share of groups the hybrid quantizer stored in symmetric mode (flag bit 0), counted
+    over the flag bits of the packed K and V caches."""
+    import torch
+    pop = torch.tensor([bin(i).count("1") for i in range(256)], dtype=torch.int64,
+                       device=caches_kv[0].device)
+    out = {}
+    for name, t in zip(("K", "V"), caches_kv):
+        f = t.view(rows, nb, fmt.block_bytes)[:, :, fmt.flag_offset:fmt.flag_offset + fmt.flag_bytes]
+        ones = int(pop[f.reshape(-1).long()].sum())
+        groups = rows * nb * 128 * 4
+        out[name] = round(1.0 - ones / groups, 5)
+    out["all"] = round((out["K"] + out["V"]) / 2, 5)
+    return out
+
+
+def warm_clocks(dev, n=1000):
+    """~100 ms of device copies (256 MB each): the GPU reaches steady clocks only after tens
+    of milliseconds of load."""
+    import torch
+    big = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+    big2 = torch.empty_like(big)
+    for _ in range(n):
+        big2.copy_(big)
+    torch.cuda.synchronize()
+    del big, big2
+
+
+def config_bench(name, args, K, S, dev, sptr, timed, cu):
+    """Step (decode + combine) and back-to-back decode of one more workload, with the same
+    rotation over cache copies as the headline figure."""
+    import numpy as np
+    import torch
+    wl = S.WORKLOADS[name]
+    fmt = K.Format(wl.bits, 128, wl.hybrid)
+    rows, bb, nb = wl.B * wl.Hkv, fmt.block_bytes, wl.n_packed // 128
+    S_ = K.suggest_splits(wl.B, wl.Hkv, wl.L, cu)
+    x = S.make_inputs(wl)
+    kps, vps = x.packed_src()
+    kr, vr = x.residual()
+    kp0 = torch.empty((rows, nb * bb), dtype=torch.uint8, device=dev)
+    vp0 = torch.empty_like(kp0)
+    for src, dst in ((kps, kp0), (vps, vp0)):
+        sd = torch.from_numpy(np.ascontiguousarray(src.reshape(rows, wl.n_packed, 128))).to(dev)
+        K.kvq_quantize_pack(fmt, sd, rows, wl.n_packed, wl.n_packed * 128, 128, dst, nb * bb, 0)
+        del sd
+    del kps, vps
+    step_bytes = wl.step_bytes()
+    copies = max(2, math.ceil(2 * MALL_BYTES / step_bytes) + 1)
+    kr_d, vr_d = torch.from_numpy(kr).to(dev), torch.from_numpy(vr).to(dev)
+    caches = [(kp0, vp0, kr_d, vr_d)] + [(kp0.clone(), vp0.clone(), kr_d.clone(), vr_d.clone())
+                                         for _ in range(copies - 1)]
+    q = torch.from_numpy(x.q).to(dev)
+    po = torch.empty((wl.B, wl.Hq, S_, 128), dtype=torch.float32, device=dev)
+    pl = torch.empty((wl.B, wl.Hq, S_), dtype=torch.float32, device=dev)
+    out = torch.empty((wl.B, wl.Hq, 128), dtype=torch.float16, device=dev)
+    sm = float(np.float32(1.0 / math.sqrt(128)))
+
+    def decode(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_decode_attention(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed, krd, vrd,
+                               128, wl.n_res, sm, S_, po, pl, stream=sp)
+
+    def step(i, sp=sptr):
+        decode(i, sp)
+        K.kvq_combine(po, pl, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+    wsn = K.kvq_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, S_)
+    ws = torch.zeros(max(wsn, 256), dtype=torch.uint8, device=dev)
+
+    def fused(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_decode_attention_fused(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed,
+                                     krd, vrd, 128, wl.n_res, sm, S_, ws, ws.numel(), out,
+                                     K.KVQ_OUT_F16, stream=sp)
+
+    n = args.per_config_steps
+    warm_clocks(dev)        # the GPU idled while the inputs were generated on the host
+    step_ms = timed(step, n, 20)
+    dec_ms = timed(decode, n, 5)
+    fused_ms = timed(fused, n, 5)
+    res = {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L, "bits": wl.bits,
+           "hybrid": wl.hybrid, "splits": S_, "cache_copies": copies,
+           "algorithmic_bytes_per_step": step_bytes,
+           "us_per_step": round(step_ms * 1e3, 3),
+           "decode_kernel_us": round(dec_ms * 1e3, 3),
+           "us_per_step_fused": round(fused_ms * 1e3, 3),
+           "GB_per_s_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
+           "GB_per_s_decode": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1),
+           "frac_step": round(step_bytes / (step_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+           "frac_decode": round(step_bytes / (dec_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
+    if wl.hybrid:
+        res["sym_mode_share"] = flag_sym_ratio(fmt, (kp0, vp0), rows, nb)
+    if wl.n_res == 128:
+        # a decode step with one appended token (folded into the decode) and the flush of
+        # the full window every 128 steps: quantize 128 tokens of every row, K and V
+        fdst = torch.empty((rows, bb), dtype=torch.uint8, device=dev)
+
+        def flush(i, sp=sptr):
+            _, _, krd, vrd = caches[i % copies]
+            K.kvq_quantize_pack(fmt, krd, rows, 128, 128 * 128, 128, fdst, bb, 0, stream=sp)
+            K.kvq_quantize_pack(fmt, vrd, rows, 128, 128 * 128, 128, fdst, bb, 0, stream=sp)
+
+        kn = torch.zeros((wl.B, wl.Hkv, 128), dtype=torch.float16, device=dev)
+
+        def serve(i, sp=sptr):
+            kp, vp, krd, vrd = caches[i % copies]
+            K.kvq_decode_attention_append(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb,
+                                          wl.n_packed, krd, vrd, 128, wl.n_res, kn, kn, sm, S_,
+                                          po, pl, stream=sp)
+            K.kvq_combine(po, pl, wl.B, wl.Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+        fl_ms = timed(flush, 50, 5)
+        sv_ms = timed(serve, n, 5)
+        res["flush_us"] = round(fl_ms * 1e3, 3)
+        res["append_decode_combine_us"] = round(sv_ms * 1e3, 3)
+        res["step_us_with_append_and_amortized_flush"] = round((sv_ms + fl_ms / 128) * 1e3, 3)
+    del caches, kp0, vp0, kr_d, vr_d
+    torch.cuda.empty_cache()
+    return res
+
+
+def stream_read_reference(K, caches, copies, step_bytes, sink, sptr, timed):
+    """The plain streaming read (kvq_stream_read) of one cache copy's bytes per launch, over
+    the same rotation as the decode: the read ceiling of this memory system for the step's
+    bytes."""
+    def rd(i, sp=sptr):
+        K.kvq_stream_read(list(caches[i % copies]), sink, stream=sp)
+    ms = timed(rd, 500, 20)
+    return {"bytes": step_bytes, "us": round(ms * 1e3, 3),
+            "GB_per_s": round(step_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac": round(step_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4)}
 
 
 def paged_bench(args, K, S, dev, stream, sptr, timed):
@@ -288,6 +451,21 @@ def main():
     dec_ms = timed(decode, args.steps, 5)
     # the VALU-only comparison kernel (same partials, no matrix cores), timed the same way
     valu_ms = timed(decode_valu, args.steps, 5)
+    # the same step as one launch: the splits merged inside the decode launch
+    # (kvq_decode_attention_fused, caller-owned workspace)
+    wsn = K.kvq_decode_workspace_bytes(wl.B, wl.Hq, wl.Hkv, S_)
+    ws = torch.zeros(max(wsn, 256), dtype=torch.uint8, device=dev)
+
+    def fused(i, sp=sptr):
+        kp, vp, krd, vrd = caches[i % copies]
+        K.kvq_decode_attention_fused(fmt, q, wl.B, wl.Hq, wl.Hkv, kp, vp, nb * bb, wl.n_packed,
+                                     krd, vrd, 128, wl.n_res, sm, S_, ws, ws.numel(), out,
+                                     K.KVQ_OUT_F16, stream=sp)
+
+    fused_ms = timed(fused, args.steps, 5)
+    # the read ceiling: a plain streaming read of the same bytes, same rotation
+    sink = torch.zeros(64, dtype=torch.int32, device=dev)
+    stream_ref = stream_read_reference(K, caches, copies, step_bytes, sink, sptr, timed)
     # the same K steps replayed from a HIP graph captured once, for reference
     cap_stream = torch.cuda.Stream(dev)
     g = torch.cuda.CUDAGraph()
@@ -476,6 +654,15 @@ def main():
         serve = {"append_decode_combine_us": round(serve3_ms * 1e3, 3),
                  "fused_append_decode_combine_us": round(serve2_ms * 1e3, 3)}
 
+    per_config = None
+    if not args.no_per_config:
+        del caches
+        torch.cuda.empty_cache()
+        cu = torch.cuda.get_device_properties(dev).multi_processor_count
+        per_config = {n: config_bench(n, args, K, S, dev, sptr, timed, cu)
+                      for n in ("tiny", "batch8_2bit_hybrid", "long_128k_3bit", "mha_b64_append")
+                      if n != wl.name}
+
     achieved = step_bytes / (dec_ms * 1e-3) / 1e9
     traffic = recorded_traffic(wl.name)
     result = {
@@ -495,6 +682,7 @@ def main():
         "pct_hbm_peak": round(100 * step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS, 2),
         "decode_kernel_us": round(dec_ms * 1e3, 3),
         "us_per_step_graph_replay": round(graph_ms * 1e3, 3),
+        "us_per_step_fused": round(fused_ms * 1e3, 3),
         "decode_kernel_valu_only_us": round(valu_ms * 1e3, 3),
         "flush_us": round(flush_ms * 1e3, 3),
         "append_us": round(append_ms * 1e3, 3),
@@ -502,6 +690,8 @@ def main():
                                                          * 1e3, 3),
         "serving_step": serve,
         "copy_reference_gbps": round(copy_gbps, 1),
+        "stream_read_reference": dict(stream_ref, decode_over_read_time=round(
+            dec_ms * 1e3 / stream_ref["us"], 3)),
         "config": {"workload": wl.name, "B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L,
                    "bits": wl.bits, "group": 32, "hybrid": wl.hybrid, "n_packed": wl.n_packed,
                    "n_res": wl.n_res, "splits": S_, "cache_copies": copies,
@@ -510,12 +700,13 @@ def main():
         "key_norm": knorm,
         "outer_grouping": outer,
         "paged": paged,
+        "per_config": per_config,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
                      "traffic": traffic, "kernel": "decode_kernel (kvq_decode_attention)"},
     }
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds)
+        result["cpu_baseline"] = cpu_baseline(wl, x, args.cpu_seconds, args.cpu_single_seconds)
     print(json.dumps(result), flush=True)
 
 

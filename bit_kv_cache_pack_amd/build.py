@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkvq.so")
 SOURCES = ["kvq_api.cpp", "quant_pack.hip", "decode_attn.hip", "decode_valu.hip", "combine.hip",
-           "keynorm.hip", "paged.hip", "quant_outer.hip"]
+           "keynorm.hip", "paged.hip", "quant_outer.hip", "stream_read.hip"]
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

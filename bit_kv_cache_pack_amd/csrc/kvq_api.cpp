@@ -395,6 +395,23 @@ kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, in
                                         out_dtype == KVQ_OUT_F16, stream));
 }
 
+kvq_status kvq_stream_read(const void *const *bufs, const int64_t *bytes, int32_t n, void *sink,
+                           hipStream_t stream)
+{
+    if (!bufs || !bytes || !sink) return KVQ_ERR_NULL;
+    if (n < 1 || n > 4) return KVQ_ERR_SHAPE;
+    int64_t pieces = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        if (!bufs[i]) return KVQ_ERR_NULL;
+        if (bytes[i] < 16 || bytes[i] % 16 != 0) return KVQ_ERR_SHAPE;
+        if (reinterpret_cast<uintptr_t>(bufs[i]) % 16 != 0) return KVQ_ERR_ALIGN;
+        pieces += (bytes[i] + 65535) / 65536;
+    }
+    if (pieces > 0x7fffffffLL) return KVQ_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(sink) % 16 != 0) return KVQ_ERR_ALIGN;
+    return launched(kvq::launch_stream_read(bufs, bytes, n, static_cast<uint32_t *>(sink), stream));
+}
+
 kvq_status kvq_append_residual(const void *k_new, const void *v_new, void *k_res, void *v_res,
                                int32_t B, int32_t Hkv, int32_t head_dim, int32_t res_capacity,
                                int32_t slot, hipStream_t stream)

@@ -74,6 +74,9 @@ hipError_t launch_decode_f16(const DecodeParams &p, hipStream_t stream);
 hipError_t launch_combine(const float *part_o, const float *part_lse, int32_t B, int32_t Hq,
                           int32_t num_splits, void *out, int32_t out_f16, hipStream_t stream);
 
+hipError_t launch_stream_read(const void *const *bufs, const int64_t *bytes, int32_t n,
+                              uint32_t *sink, hipStream_t stream);
+
 hipError_t launch_append(const uint16_t *k_new, const uint16_t *v_new, uint16_t *k_res,
                          uint16_t *v_res, int32_t B, int32_t Hkv, int32_t res_cap, int32_t slot,
                          hipStream_t stream);

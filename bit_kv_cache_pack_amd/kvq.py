@@ -31,7 +31,7 @@ EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_k
             "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
             "kvq_decode_attention_outer", "kvq_decode_attention_append",
             "kvq_decode_attention_fused", "kvq_decode_attention_paged_fused",
-            "kvq_decode_attention_fused_noalloc")
+            "kvq_decode_attention_fused_noalloc", "kvq_stream_read")
 # exported calls that return a size rather than a status
 EXPORTED_SIZE = ("kvq_decode_workspace_bytes",)
 
@@ -122,6 +122,7 @@ def lib():
         L.kvq_decode_attention_append.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i32, vp,
                                                   vp, i32, i32, vp, vp, f32, i32, vp, vp, vp]
         L.kvq_append_residual.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+        L.kvq_stream_read.argtypes = [C.POINTER(vp), C.POINTER(i64), i32, vp, vp]
         L.kvq_key_norm.argtypes = [vp, i64, i32, i64, i64, i32, vp, vp]
         L.kvq_channel_scale.argtypes = [vp, i64, i32, i64, i64, i32, vp, i64, i32, vp, i64, i64,
                                         vp]
@@ -283,6 +284,15 @@ def kvq_append_residual(k_new, v_new, k_res, v_res, B: int, Hkv: int, head_dim: 
     st = lib().kvq_append_residual(_ptr(k_new), _ptr(v_new), _ptr(k_res), _ptr(v_res), B, Hkv,
                                    head_dim, res_capacity, slot, _stream(stream, k_new))
     _check("kvq_append_residual", st)
+
+
+def kvq_stream_read(bufs, sink, stream=None):
+    """One streaming read of the device buffers `bufs` (1..4 tensors, read whole)."""
+    n = len(bufs)
+    ptrs = (C.c_void_p * n)(*[_ptr(b) for b in bufs])
+    sizes = (C.c_int64 * n)(*[b.numel() * b.element_size() for b in bufs])
+    st = lib().kvq_stream_read(ptrs, sizes, n, _ptr(sink), _stream(stream, sink))
+    _check("kvq_stream_read", st)
 
 
 def kvq_key_norm(k_fp16, n_rows: int, n_tokens: int, row_stride: int, tok_stride: int,

@@ -614,6 +614,20 @@ kvq_status kvq_decode_attention_paged_fused(const kvq_format *fmt, const void *q
                                             int64_t workspace_bytes, void *out, int32_t out_dtype,
                                             hipStream_t stream);
 
+/*
+ * kvq_stream_read -- a measurement reference, not part of the method: read n (1..4) device
+ * buffers once, as one streaming pass with plain 16-byte non-temporal loads (every 64 KB
+ * piece of a buffer one workgroup of 256 threads, all of a thread's loads in flight at
+ * once), and nothing else. Timed over the bytes a decode step reads, it gives the read
+ * bandwidth the same memory system delivers to a kernel with no other work.
+ *   bufs, bytes     host arrays of n device pointers (16-byte aligned) and byte counts
+ *                   (multiples of 16, at least 16 each; at most 2^31 - 1 pieces in all)
+ *   sink            device memory of at least 256 bytes; written only in the practically
+ *                   impossible case that a workgroup's folded data equals a fixed constant
+ */
+kvq_status kvq_stream_read(const void *const *bufs, const int64_t *bytes, int32_t n, void *sink,
+                           hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

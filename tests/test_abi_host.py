@@ -160,6 +160,28 @@ def test_append_rejects(args, status):
     assert K.lib().kvq_append_residual(*args, None) == status
 
 
+def _sr(bufs=(A, A), sizes=(4096, 4096), n=None, sink=A):
+    n = len(bufs) if n is None else n
+    arr_p = (C.c_void_p * max(1, len(bufs)))(*bufs)
+    arr_s = (C.c_int64 * max(1, len(sizes)))(*sizes)
+    return K.lib().kvq_stream_read(arr_p, arr_s, n, sink, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bufs=(A, None)), K.KVQ_ERR_NULL),
+    (dict(sink=None), K.KVQ_ERR_NULL),
+    (dict(n=0), K.KVQ_ERR_SHAPE),
+    (dict(bufs=(A,) * 5, sizes=(4096,) * 5), K.KVQ_ERR_SHAPE),
+    (dict(sizes=(4096, 0)), K.KVQ_ERR_SHAPE),
+    (dict(sizes=(4096, 4100)), K.KVQ_ERR_SHAPE),
+    (dict(sizes=(4096, 1 << 62)), K.KVQ_ERR_SHAPE),
+    (dict(bufs=(A, A + 8)), K.KVQ_ERR_ALIGN),
+    (dict(sink=A + 4), K.KVQ_ERR_ALIGN),
+])
+def test_stream_read_rejects(kw, status):
+    assert _sr(**kw) == status
+
+
 @pytest.mark.parametrize("bits,hybrid", [(2, 0), (2, 1), (3, 0), (3, 1), (4, 0), (4, 1)])
 def test_format_sizes_agree_with_oracle_restatement(oracle_mod, bits, hybrid):
     """The header's size helpers (mirrored in Python) and the oracle's independent

@@ -130,6 +130,40 @@ def test_decode_single_token(oracle_mod):
     assert np.max(np.abs(got - vr[0, 0, 0].astype(np.float32)[None, None])) <= 1e-6
 
 
+@pytest.mark.parametrize("bits,n_res,S_,B", [(4, 1, 1, 1), (4, 40, 1, 1), (3, 5, 2, 1),
+                                              (2, 1, 1, 1), (4, 33, 3, 1), (4, 1, 1, 300),
+                                              (3, 40, 1, 300)])
+def test_decode_window_far_below_packed(oracle_mod, bits, n_res, S_, B):
+    """Window keys point away from q and packed keys towards it, so a wave's first packed
+    tile raises the running max far beyond the lazy rescale's slack after its window tile
+    has been taken: the window's P V (weight ~e^-40 in the result) must be rescaled with
+    the rest, whichever of the two a wave takes first."""
+    from gpu_common import assert_close, dev, gpu_decode, gpu_quantize
+    O = oracle_mod
+    rng = np.random.default_rng(100 + bits + n_res + S_ + B)
+    Hq, Hkv, n_packed, cap = 4, 1, 256, 128
+    u = rng.standard_normal(128)
+    q = _f16(u[None, None, :] + 0.1 * rng.standard_normal((B, Hq, 128)))
+    kp_src = _f16(rng.standard_normal((B * Hkv, n_packed, 128)) + 1.2 * u)
+    vp_src = _f16(rng.standard_normal((B * Hkv, n_packed, 128)))
+    kr = np.zeros((B, Hkv, cap, 128), np.float16)
+    vr = np.zeros_like(kr)
+    kr[:, :, :n_res] = _f16(rng.standard_normal((B, Hkv, n_res, 128)) - 1.2 * u)
+    vr[:, :, :n_res] = _f16(rng.standard_normal((B, Hkv, n_res, 128)) * 4.0)
+    fmt, ofmt = K.Format(bits), O.Format(bits)
+    print(f"[window below packed] bits={bits} n_res={n_res} S={S_} B={B}", flush=True)
+    kp_ref = O.quantize_pack(ofmt, kp_src)
+    vp_ref = O.quantize_pack(ofmt, vp_src)
+    kp, vp = gpu_quantize(fmt, kp_src), gpu_quantize(fmt, vp_src)
+    out, po, pl = gpu_decode(fmt, dev(q), Hkv, kp, vp, n_packed, dev(kr), dev(vr), n_res, S_, sm=SM)
+    torch.cuda.synchronize()
+    ref = O.attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, sm=SM)
+    assert_close(out.cpu().numpy(), ref, "attention")
+    rpo, rpl = O.split_attention(ofmt, q, Hkv, kp_ref, vp_ref, n_packed, kr, vr, n_res, S=S_, sm=SM)
+    empty = np.isneginf(rpl)
+    assert_close(po.cpu().numpy()[~empty], rpo[~empty], "partials")
+
+
 def test_combine_alone_matches_oracle(oracle_mod):
     """kvq_combine on partials made by the oracle (fp64 -> fp32), against the oracle merge."""
     from gpu_common import DEV, assert_close
