@@ -12,7 +12,8 @@ import os
 from dataclasses import dataclass
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libkvq.so")
+# KVQ_LIB_PATH may name another build of the same ABI (the sanitizer-checked host build)
+LIB_PATH = os.environ.get("KVQ_LIB_PATH") or os.path.join(PKG, "libkvq.so")
 
 KVQ_OK, KVQ_ERR_NULL, KVQ_ERR_SHAPE, KVQ_ERR_UNSUPPORTED, KVQ_ERR_ALIGN, KVQ_ERR_LAUNCH = \
     0, -1, -2, -3, -4, -5

@@ -14,7 +14,8 @@ from dataclasses import dataclass
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# KVQ_ORACLE_LIB_PATH may name another build of the oracle (the sanitizer-checked one)
+_LIB_PATH = os.environ.get("KVQ_ORACLE_LIB_PATH") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 GROUP = 32

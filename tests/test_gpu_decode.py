@@ -236,6 +236,8 @@ def _random_cases(n, seed=2024):
         cap = int(rng.choice([32, 64, 100, 128]))
         n_res = int(rng.integers(0 if n_packed else 1, cap + 1))
         S_ = int(rng.choice([1, 2, 3, 5, 8, 16, 33]))
+        if i % 8 == 3:          # every eighth draw: packed tokens and an empty window
+            n_packed, n_res = max(n_packed, 128), 0
         out.append((i, bits, hybrid, B, gq * Hkv, Hkv, n_packed, n_res, cap, S_))
     return out
 
@@ -248,8 +250,8 @@ def test_decode_random_shapes(oracle_mod, case):
     i, bits, hybrid, B, Hq, Hkv, n_packed, n_res, cap, S_ = case
     _run(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, seed=500 + i, cap=cap)
     if n_res >= 1:
-        test_decode_append_equals_append_then_decode(
-            oracle_mod, (bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S_))
+        _append_check(oracle_mod, (bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S_),
+                      seed=500 + i)
 
 
 APPEND_CASES = [
@@ -270,10 +272,14 @@ def test_decode_append_equals_append_then_decode(oracle_mod, case):
     """kvq_decode_attention_append equals kvq_append_residual into slot n_res - 1 followed by
     kvq_decode_attention: the same window afterwards and the same partials, bit for bit;
     and the merged output matches the oracle on the updated cache."""
+    _append_check(oracle_mod, case, seed=300 + case[7])
+
+
+def _append_check(oracle_mod, case, seed):
     from gpu_common import DEV, assert_close, dev, gpu_quantize
     O = oracle_mod
     bits, hybrid, B, Hq, Hkv, n_packed, cap, n_res, S_ = case
-    rng = np.random.default_rng(300 + n_res)
+    rng = np.random.default_rng(seed)
     rows = B * Hkv
     fmt, ofmt = K.Format(bits, 128, hybrid), O.Format(bits, 128, hybrid)
     q = _f16(rng.standard_normal((B, Hq, 128)))
@@ -281,7 +287,7 @@ def test_decode_append_equals_append_then_decode(oracle_mod, case):
     vr = _f16(rng.standard_normal((B, Hkv, cap, 128)))
     kn = _f16(rng.standard_normal((B, Hkv, 128)) * 2)
     vn = _f16(rng.standard_normal((B, Hkv, 128)) * 2)
-    print(f"[decode append] case={case}", flush=True)
+    print(f"[decode append] case={case} seed={seed}", flush=True)
     if n_packed:
         ks = _f16(rng.standard_normal((rows, n_packed, 128)))
         vs = _f16(rng.standard_normal((rows, n_packed, 128)))
