@@ -49,6 +49,7 @@
 namespace kvq {
 namespace {
 
+
 // LDS of one workgroup: a RING-slot ring of tiles per wave plus small staging arrays
 // (4-bit: ~49 KB with 2 slots, three workgroups per CU).
 // A wave's merge output (mo) reuses the start of its own ring once its tiles are done.
@@ -76,6 +77,22 @@ __device__ __forceinline__ void pair_tokens(uint32_t a, uint32_t b, const Magic 
 // values (p, scale_v) are stored at the slot position pos(t) = 8 * (t % 4) + t / 4 so that
 // lane group r reads its eight values as two contiguous 16-byte words.
 __device__ __forceinline__ int slot_pos(int t) { return 8 * (t & 3) + (t >> 2); }
+// Position of token t's p in row h of a wave's p buffer. Odd rows swap the two 4-float
+// halves of every 8-float block: the slots of tokens 0..15 (and those of 16..31) then sit
+// on different banks in rows 2i and 2i+1, so neither the 32-lane stores of p nor the
+// 16-byte reads of load_p8 meet a bank conflict (measured with the LDS counters).
+__device__ __forceinline__ int p_pos(int h, int t) { return h * kTile + (slot_pos(t) ^ (4 * (h & 1))); }
+
+// The packed kernel's q in LDS, as 64 pieces of 16 bytes (8 channels): channels
+// 32 r + 8 o .. +7 of head h sit in piece 32 (o / 2) + 8 h + 2 r + o % 2. For one o the
+// 16 pieces the lanes (head h, group r) read then lie as the p reads of load_p8 do, with
+// no bank conflict (the plain head-major order has four-way conflicts there).
+__device__ __forceinline__ int q_piece(int h, int r, int o) { return 32 * (o >> 1) + 8 * h + 2 * r + (o & 1); }
+// the head-major piece (16 h + 4 r + o) that piece p of the LDS order holds
+__device__ __forceinline__ int q_piece_src(int p)
+{
+    return 16 * ((p & 31) >> 3) + 4 * ((p & 7) >> 1) + 2 * (p >> 5) + (p & 1);
+}
 
 // v[k] for a lane-varying k in 0..3, as two levels of selects (a runtime vector index
 // would otherwise go through scratch memory)
@@ -143,8 +160,9 @@ __device__ __forceinline__ void softmax_a(const float lg[2], const float zv[2][4
 __device__ __forceinline__ void load_p8(const float *pw, int n, int r, float p8[8])
 {
     const int hA = n >> 2;
-    const float4_t pl = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r);
-    const float4_t ph = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r + 4);
+    const int sw = 4 * (hA & 1);     // the half swap of odd rows (p_pos)
+    const float4_t pl = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r + sw);
+    const float4_t ph = *reinterpret_cast<const float4_t *>(pw + hA * kTile + 8 * r + (4 - sw));
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         p8[e] = pl[e];
@@ -254,8 +272,8 @@ __device__ __forceinline__ void stage_a_packed(const uint8_t *slot, float *pw, c
     const bool big_scale = __builtin_amdgcn_ballot_w64(big) != 0;
     float p0, p1;
     softmax_a(lg, zv, big_scale, st, p0, p1, alpha, rescale);
-    pw[r * kTile + slot_pos(n)] = p0;
-    pw[r * kTile + slot_pos(16 + n)] = p1;
+    pw[p_pos(r, n)] = p0;
+    pw[p_pos(r, 16 + n)] = p1;
 }
 
 __device__ __forceinline__ void rescale_pv(WaveState &st, float alpha)
@@ -306,7 +324,7 @@ __device__ __forceinline__ void stage_a_outer(const uint8_t *slot, float *pw, co
 #pragma unroll
     for (int o = 0; o < 4; ++o) {
         const int c0 = 32 * r + 8 * o;
-        const u32x4 qv = *reinterpret_cast<const u32x4 *>(qw + hA * kHeadDim + c0);
+        const u32x4 qv = *reinterpret_cast<const u32x4 *>(qw + 8 * q_piece(hA, r, o));
         const u32x4 s0 = *reinterpret_cast<const u32x4 *>(slot + G::KSZ + c0 * 4);
         const u32x4 s1 = *reinterpret_cast<const u32x4 *>(slot + G::KSZ + c0 * 4 + 16);
         u32x4 hi, lo;
@@ -351,8 +369,8 @@ __device__ __forceinline__ void stage_a_outer(const uint8_t *slot, float *pw, co
     float p0, p1;
     softmax_a(lg, zv, false, st, p0, p1, alpha, rescale);
     pv.P = row_sum16(p0 + p1);
-    pw[r * kTile + slot_pos(n)] = p0;
-    pw[r * kTile + slot_pos(16 + n)] = p1;
+    pw[p_pos(r, n)] = p0;
+    pw[p_pos(r, 16 + n)] = p1;
 }
 
 template <int BITS>
@@ -500,7 +518,8 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t rr, int rec, fl
                                               kScDevice);
 }
 
-// merge records first .. first + cnt - 1 (cnt <= 8) into (v0, v1, lse2)
+// merge records first .. first + cnt - 1 (cnt <= kFanIn) into (v0, v1, lse2); all of a
+// thread's loads are issued before the first is used (one memory round trip)
 __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, int cnt, float &v0,
                                           float &v1, float &lse2)
 {
@@ -510,10 +529,10 @@ __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, 
     if (threadIdx.x >= 256) return;
     const int h = threadIdx.x >> 6;
     const int d = (threadIdx.x & 63) * 2;
-    u32x2 x[8];
-    uint32_t lb[8];
+    u32x2 x[kFanIn];
+    uint32_t lb[kFanIn];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < kFanIn; ++j) {
         const int rec = first + (j < cnt ? j : 0);
         x[j] = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
                                                     0, kScDevice);
@@ -522,12 +541,12 @@ __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, 
     }
     float M = -INFINITY;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < kFanIn; ++j)
         if (j < cnt) M = fmaxf(M, __uint_as_float(lb[j]));
     float a0 = 0.f, a1 = 0.f, ws = 0.f;
     if (M != -INFINITY) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
+        for (int j = 0; j < kFanIn; ++j) {
             if (j < cnt) {
                 const float w = __builtin_amdgcn_exp2f(__uint_as_float(lb[j]) - M);
                 a0 += w * __uint_as_float(x[j][0]);
@@ -579,9 +598,9 @@ __device__ __forceinline__ void merge_fused(SM &sm, const WaveState &st, int wav
     int n_lvl = a.S, idx = split, rec0 = 0;
     rec_store(rr, idx, v0, v1, lse2);
     for (;;) {
-        const int parent = idx >> 3, first = parent << 3;
-        const int cnt = n_lvl - first < 8 ? n_lvl - first : 8;
-        const int n_up = (n_lvl + 7) >> 3;
+        const int parent = idx / kFanIn, first = parent * kFanIn;
+        const int cnt = n_lvl - first < kFanIn ? n_lvl - first : kFanIn;
+        const int n_up = (n_lvl + kFanIn - 1) / kFanIn;
         if (cnt > 1) {
             asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this record is stored
             __syncthreads();
@@ -708,7 +727,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
     // reusing such a register)
     if (wave == 0) {
         dma(rq, reinterpret_cast<uint8_t *>(&sm.q[0][0][0]),
-            (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + lane * 16, 16);
+            (uint32_t)(((int64_t)b * a.Hq + h0) * kHeadDim * 2) + q_piece_src(lane) * 16, 16);
         if (a.qnorm && lane < 32) {
             const __amdgpu_buffer_rsrc_t rn = __builtin_amdgcn_make_buffer_rsrc(
                 const_cast<float *>(a.qnorm + row * kHeadDim), 0, kHeadDim * 4, kRsrcWord3);
@@ -731,7 +750,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
     if (wave == 0 && a.qnorm) {
         // q' = fp16(q * norm) per channel: lane (r, n) rescales the 16 bytes it loaded
         // (head r of the chunk, channels 8n..8n+7) in place
-        u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.q[0][r][8 * n]);
+        u32x4 *mine = reinterpret_cast<u32x4 *>(&sm.q[0][0][0]) + q_piece(r, n >> 2, n & 3);
         const u32x4 w = *mine;
         const float4_t qn0 = *reinterpret_cast<const float4_t *>(&sm.qn[8 * n]);
         const float4_t qn1 = *reinterpret_cast<const float4_t *>(&sm.qn[8 * n + 4]);
@@ -763,7 +782,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         const bool live = (gA == r) && (hA < NH);
 #pragma unroll
         for (int o = 0; o < 4; ++o) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(&sm.q[0][hA][32 * r + 8 * o]);
+            const u32x4 w = reinterpret_cast<const u32x4 *>(&sm.q[0][0][0])[q_piece(hA, r, o)];
             half8_t h = live ? perm_octet_f16(w) : half8_t{};
             if (weighted) {
 #pragma unroll
@@ -782,7 +801,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         // lane (hh, gg, qq) sums 8 channels; the quad sum is Qs[hh][gg]; lane (n, r) then
         // fetches Qs[r][g] from lane 16r + 4g
         const int hh = lane >> 4, gg = (lane >> 2) & 3, qq = lane & 3;
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(&sm.q[0][hh][gg * 32 + qq * 8]);
+        const u32x4 v = reinterpret_cast<const u32x4 *>(&sm.q[0][0][0])[q_piece(hh, gg, qq)];
         float s = 0.0f;
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -945,8 +964,8 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
             bool resc;
             softmax_a(lg, zv, false, st, p0, p1, alpha, resc);
             if (resc) rescale_pv(st, alpha);
-            pbuf[r * kTile + slot_pos(n)] = p0;
-            pbuf[r * kTile + slot_pos(16 + n)] = p1;
+            pbuf[p_pos(r, n)] = p0;
+            pbuf[p_pos(r, 16 + n)] = p1;
             lds_fence();
             float p8[8];
             load_p8(pbuf, n, r, p8);
@@ -1092,8 +1111,8 @@ __global__ __launch_bounds__(64 * W) void decode_f16_kernel(DecArgs a)
         bool resc;
         softmax_a(lg, zv, false, st, p0, p1, alpha, resc);
         if (resc) rescale_pv(st, alpha);
-        pbuf[r * kTile + slot_pos(n)] = p0;
-        pbuf[r * kTile + slot_pos(16 + n)] = p1;
+        pbuf[p_pos(r, n)] = p0;
+        pbuf[p_pos(r, 16 + n)] = p1;
         lds_fence();
         float p8[8];
         load_p8(pbuf, n, r, p8);

@@ -109,9 +109,15 @@ __device__ __forceinline__ void issue_tile_at(__amdgpu_buffer_rsrc_t rk, __amdgp
             dma_nt(rv, slot + G::CB + 1024, c0 + 1024 + lane * 16);
         }
     } else {
+        // 4-bit K codes: each 1 KB request (16 tokens x 64 B) lands transposed in LDS, the
+        // 16-byte piece of group r of token n at position 16 r + n (KGroup<4>::load), so
+        // that the 128-bit reads of one group for 16 tokens are consecutive in LDS (no bank
+        // conflict); the request still reads the same whole 1 KB
+        const uint32_t koff = BITS == 4 ? (uint32_t)(64 * (lane & 15) + 16 * (lane >> 4))
+                                        : (uint32_t)lane * 16u;
 #pragma unroll
         for (int k = 0; k < G::CB / 1024; ++k) {
-            dma_nt(rk, slot + 1024 * k, c0 + 1024 * k + lane * 16);
+            dma_nt(rk, slot + 1024 * k, c0 + 1024 * k + koff);
             dma_nt(rv, slot + G::CB + 1024 * k, c0 + 1024 * k + lane * 16);
         }
     }
@@ -178,9 +184,11 @@ struct KGroup;
 template <>
 struct KGroup<4> {
     u32x4 w;
+    // group r of token t: piece 16 r + t % 16 of the tokens' 1 KB half (the transposed
+    // order issue_tile_at writes)
     __device__ __forceinline__ void load(const uint8_t *slot, int t, int r)
     {
-        w = *reinterpret_cast<const u32x4 *>(slot + t * 64 + r * 16);
+        w = *reinterpret_cast<const u32x4 *>(slot + (t >> 4) * 1024 + r * 256 + (t & 15) * 16);
     }
     __device__ __forceinline__ half8_t octet(int o, const Magic &M) const { return unpack_octet4(w[o], M); }
     __device__ __forceinline__ half8_t raw(int o) const { return raw_octet4(w[o]); }

@@ -43,10 +43,15 @@ struct DecodeParams {
 // Workspace of the fused split merge: per group (a row's chunk of up to 4 query heads) one
 // 2080-byte slot per node below the root of the fan-in-8 split tree (a record, plus the
 // counter of the node's parent in the padding of its first child's slot).
+#ifndef KVQ_FANIN
+#define KVQ_FANIN 8
+#endif
+constexpr int32_t kFanIn = KVQ_FANIN;     // children per node of the split tree
+
 inline int32_t fused_records(int32_t S)
 {
     int32_t r = 0;
-    for (int32_t n = S; n > 1; n = (n + 7) / 8) r += n;
+    for (int32_t n = S; n > 1; n = (n + kFanIn - 1) / kFanIn) r += n;
     return r;
 }
 inline int64_t fused_workspace_bytes(int32_t B, int32_t Hq, int32_t Hkv, int32_t S)
