@@ -304,6 +304,7 @@ def paged_bench(args, K, S, dev, stream, sptr, timed):
     st0 = np.zeros((B, 4), np.int32)
     st0[:, 0], st0[:, 1], st0[:, 2] = x.n_packed, x.n_res, 0
     state0 = torch.from_numpy(st0).to(dev)
+    st_init = state0.clone()
     caches = [(kpool, vpool, kr0, vr0, state0)] + [
         (kpool.clone(), vpool.clone(), kr0.clone(), vr0.clone(), state0.clone())
         for _ in range(copies - 1)]
@@ -326,22 +327,93 @@ def paged_bench(args, K, S, dev, stream, sptr, timed):
         K.kvq_append_evict(fmt, kn, kn, krd, vrd, cap, 0, kp, vp, npool, bs, hs, tbl, maxb, st,
                            B, Hkv, stream=sp)
 
-    def step(i, sp=sptr):
+    def step_separate(i, sp=sptr):
         update(i, sp)
         decode(i, sp)
         K.kvq_combine(po, pl, B, Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
 
-    # every sequence grows by one packed token per update: at most 204 updates over >= 2
-    # cache copies stay within the spare block
-    steps = min(args.steps, 100)
-    step_ms = timed(step, steps, 2)
-    dec_ms = timed(decode, args.steps, 5)
-    upd_ms = timed(update, min(args.steps, 100), 2)
+    # the folded step: kvq_decode_attention_paged_append applies the update inside the
+    # decode; it reads a state buffer and writes the next one, so every copy keeps two and
+    # alternates between them
+    alt = [st.clone() for (_, _, _, _, st) in caches]
+    cur = [0] * copies
+
+    def fold(i, sp=sptr):
+        c = i % copies
+        kp, vp, krd, vrd, st = caches[c]
+        s_in, s_out = (st, alt[c]) if cur[c] == 0 else (alt[c], st)
+        K.kvq_decode_attention_paged_append(fmt, q, B, Hq, Hkv, kp, vp, npool, bs, hs, tbl, maxb,
+                                            s_in, s_out, krd, vrd, cap, 0, kn, kn, sm, S_, po,
+                                            pl, stream=sp)
+        cur[c] ^= 1
+
+    def combine(i, sp=sptr):
+        K.kvq_combine(po, pl, B, Hq, 128, S_, out, K.KVQ_OUT_F16, stream=sp)
+
+    def step(i, sp=sptr):
+        fold(i, sp)
+        combine(i, sp)
+
+    # one step both ways from the same cache (copies 0 and 1 are equal before any step):
+    # partials, pools, windows and states must agree bit for bit
+    step_separate(0)
+    po_s, pl_s = po.clone(), pl.clone()
+    step(1)
+    torch.cuda.synchronize()
+    a, b_ = caches[0], caches[1]
+    identical = bool(torch.equal(po_s, po) and torch.equal(pl_s, pl) and
+                     all(torch.equal(u, v) for u, v in zip(a[:4], b_[:4])) and
+                     torch.equal(a[4], alt[1]))
+    del po_s, pl_s
+
+    wsb = K.kvq_decode_workspace_bytes(B, Hq, Hkv, S_)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+
+    def decode_fused(i, sp=sptr):
+        kp, vp, krd, vrd, st = caches[i % copies]
+        K.kvq_decode_attention_paged_fused(fmt, q, B, Hq, Hkv, kp, vp, npool, bs, hs, tbl, maxb,
+                                           st, krd, vrd, cap, sm, S_, ws, wsb, out,
+                                           K.KVQ_OUT_F16, stream=sp)
+
+    def reset():
+        # every copy back to the starting lengths (the pool and window bytes an update
+        # wrote stay; the next updates write the same positions again)
+        for c in range(copies):
+            caches[c][4].copy_(st_init)
+            alt[c].copy_(st_init)
+            cur[c] = 0
+
+    # every sequence grows by one packed token per update and its spare block holds 128:
+    # the states are reset before each timed loop that updates. The loops run in rounds,
+    # interleaved, and each figure is the median over the rounds (the clock drifts by a
+    # few percent over a run).
+    n = min(args.steps, 40)
+    meas = {k: [] for k in ("step", "sep", "fold", "dec", "comb", "decf", "upd")}
+    for _ in range(5):
+        reset()
+        meas["dec"].append(timed(decode, n, 3))
+        meas["fold"].append(timed(fold, n, 2))
+        reset()
+        meas["step"].append(timed(step, n, 2))
+        reset()
+        meas["sep"].append(timed(step_separate, n, 2))
+        reset()
+        meas["upd"].append(timed(update, n, 2))
+        meas["comb"].append(timed(combine, n, 3))
+        meas["decf"].append(timed(decode_fused, n, 3))
+    med = {k: float(np.median(v)) for k, v in meas.items()}
+    step_ms, sep_ms, fold_ms, dec_ms = med["step"], med["sep"], med["fold"], med["dec"]
+    comb_ms, decf_ms, upd_ms = med["comb"], med["decf"], med["upd"]
     res = {"workload": pw.name, "B": B, "Hq": Hq, "Hkv": Hkv, "bits": pw.bits,
            "lengths": [int(v) for v in (x.n_packed + x.n_res)], "splits": S_,
            "cache_copies": copies, "step_bytes": step_bytes,
            "us_per_step": round(step_ms * 1e3, 3),
+           "us_per_step_separate_update": round(sep_ms * 1e3, 3),
+           "folded_step_bit_identical": identical,
            "decode_kernel_us": round(dec_ms * 1e3, 3),
+           "decode_append_kernel_us": round(fold_ms * 1e3, 3),
+           "combine_us": round(comb_ms * 1e3, 3),
+           "decode_fused_us": round(decf_ms * 1e3, 3),
            "append_evict_us": round(upd_ms * 1e3, 3),
            "GB_per_s_step": round(step_bytes / (step_ms * 1e-3) / 1e9, 1),
            "GB_per_s_decode": round(step_bytes / (dec_ms * 1e-3) / 1e9, 1),
@@ -600,9 +672,11 @@ def main():
     del kps_d
 
     # paged cache: a serving-shaped batch of ragged sequences whose blocks are scattered
-    # over one pool. One step = kvq_append_evict (the new token of every sequence enters
-    # its window, evicting the oldest recent token into the packed cache) +
-    # kvq_decode_attention_paged + kvq_combine. Bytes = the step's algorithmic decode bytes.
+    # over one pool. One step = kvq_decode_attention_paged_append (the new token of every
+    # sequence enters its window, evicting the oldest recent token into the packed cache,
+    # inside the decode launch) + kvq_combine; the same step as three calls
+    # (kvq_append_evict, kvq_decode_attention_paged, kvq_combine) is reported beside it.
+    # Bytes = the step's algorithmic decode bytes.
     paged = None
     if not args.no_paged:
         paged = paged_bench(args, K, S, dev, stream, sptr, timed)

@@ -40,6 +40,8 @@
 #include "decode_common.h"
 #include "kvq.h"
 #include "kvq_internal.h"
+#include "paged_common.h"
+#include "quant_common.h"
 
 #include <math.h>
 
@@ -60,6 +62,9 @@ struct Smem {
     alignas(16) float qn[kHeadDim];                    // the row's key-channel norms (if any)
     alignas(16) float p[W][2][4][kTile];      // p of head h, token t of tiles 2j and 2j+1
     alignas(16) float ml[W][4][2];
+    // paged update: K and V of the token leaving the window ([0], [1]) and of the new one ([2], [3])
+    alignas(16) uint16_t ev[4][kHeadDim];
+    uint32_t evc[2][16], evs[2][4];           // its code words and scale/zero words
     uint32_t flag;                            // last-arrival flag of the fused split merge
     __device__ __forceinline__ float *mo(int w) { return reinterpret_cast<float *>(&ring[w][0][0]); }
 };
@@ -431,7 +436,7 @@ __device__ __forceinline__ void merge_waves(SM &sm, const WaveState &st, int wav
     }
     __syncthreads();
     const int h = threadIdx.x >> 6;       // 4 heads x 64 threads x 2 channels
-    const int d = (threadIdx.x & 63) * 2;
+    const int d = 2 * lane_full();
     v0 = 0.f;
     v1 = 0.f;
     lse2 = -INFINITY;
@@ -468,7 +473,7 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
     float v0, v1, lse2;
     merge_waves<NH, W>(sm, st, wave, n, r, v0, v1, lse2);
     const int h = threadIdx.x >> 6;
-    const int d = (threadIdx.x & 63) * 2;
+    const int d = 2 * lane_full();
     if (h < NH) {
         const int64_t hq = hq0 + h;
         const int64_t ob = (hq * S + split) * kHeadDim + d;
@@ -508,7 +513,7 @@ __device__ __forceinline__ void rec_store(__amdgpu_buffer_rsrc_t rr, int rec, fl
 {
     if (threadIdx.x >= 256) return;
     const int h = threadIdx.x >> 6;
-    const int d = (threadIdx.x & 63) * 2;
+    const int d = 2 * lane_full();
     const u32x2 v = {__float_as_uint(v0), __float_as_uint(v1)};
     __builtin_amdgcn_raw_buffer_store_b64(v, rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
                                           0, kScDevice);
@@ -528,7 +533,7 @@ __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, 
     lse2 = -INFINITY;
     if (threadIdx.x >= 256) return;
     const int h = threadIdx.x >> 6;
-    const int d = (threadIdx.x & 63) * 2;
+    const int d = 2 * lane_full();
     u32x2 x[kFanIn];
     uint32_t lb[kFanIn];
 #pragma unroll
@@ -571,7 +576,7 @@ template <int NH>
 __device__ __forceinline__ void out_store(const DecArgs &a, int64_t hq0, float v0, float v1)
 {
     const int h = threadIdx.x >> 6;
-    const int d = (threadIdx.x & 63) * 2;
+    const int d = 2 * lane_full();
     if (h >= NH) return;
     const int64_t o = (hq0 + h) * kHeadDim + d;
     if (a.out_f16) {
@@ -662,9 +667,33 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
 
     // ---- this sequence's lengths (a paged cache has its own per sequence) ----
     int n_packed_b = a.n_packed, n_res_b = a.n_res;
+    int upd_slot = -1;      // update calls: the window slot the new token takes
+    int ev_pos = -1;        // update calls that evict: the packed position of the evicted token
     if constexpr (PAGED) {
         n_packed_b = __builtin_amdgcn_readfirstlane(seq_state[4 * (int64_t)b]);
         n_res_b = __builtin_amdgcn_readfirstlane(seq_state[4 * (int64_t)b + 1]);
+        if (a.upd) {
+            // the step's update, as kvq_append_evict applies it (same clamping of a state
+            // outside its range): the new token takes slot n_res while the window has room;
+            // otherwise the token in slot next_slot moves to packed position n_packed and
+            // the new token takes its slot. Attention then covers the updated lengths.
+            const int nxt = __builtin_amdgcn_readfirstlane(seq_state[4 * (int64_t)b + 2]);
+            const bool full = n_res_b >= a.res_cap;
+            int slot = full ? nxt : (n_res_b < 0 ? 0 : n_res_b);
+            if (full && (slot < a.n_sink || slot >= a.res_cap)) slot = a.n_sink;
+            upd_slot = slot;
+            const int n_packed_new = full ? n_packed_b + 1 : n_packed_b;
+            const int n_res_new = full ? a.res_cap : slot + 1;
+            if (full) ev_pos = n_packed_b;
+            if (kvh == 0 && split == 0 && blockIdx.z == 0 && a.head_base == 0 && threadIdx.x == 0) {
+                const int pad = seq_state[4 * (int64_t)b + 3];
+                const int nxt_new = full ? (slot + 1 < a.res_cap ? slot + 1 : a.n_sink) : nxt;
+                *reinterpret_cast<int4 *>(a.state_out + 4 * (int64_t)b) =
+                    int4{n_packed_new, n_res_new, nxt_new, pad};
+            }
+            n_packed_b = n_packed_new;
+            n_res_b = n_res_new;
+        }
         // out-of-range lengths are clamped (never an access outside the table or window)
         const int cap_p = a.max_blocks * kBlockTokens;
         n_packed_b = n_packed_b < 0 ? 0 : (n_packed_b > cap_p ? cap_p : n_packed_b);
@@ -683,6 +712,13 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         const_cast<uint8_t *>(a.kp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
     const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint8_t *>(a.vp + row * a.row_stride), 0, a.row_bytes, kRsrcWord3);
+    // the last tile of a ragged sequence: tokens nv_last .. 31 are past the sequence's end
+    // (the pool bytes behind them may be anything). Their scale/zero words are loaded as
+    // zeros (the block's buffer range ends at the last valid token's scale/zero word, and a
+    // direct-to-LDS load past the range writes zeros), so their K and V dequantize to 0;
+    // they are also masked out of the softmax.
+    const int nt_seq = (n_packed_b + kTile - 1) / kTile;
+    const int nv_last = n_packed_b - (nt_seq - 1) * kTile;
     // request tile `tile` of this row into `slot`: from the contiguous row, or from the
     // pool block the table names (a block id outside the pool reads block 0 instead)
     auto issue = [&](uint8_t *slot, int tile) {
@@ -690,27 +726,99 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
             int64_t blk = __builtin_amdgcn_readfirstlane(tbl[(int64_t)b * a.max_blocks + (tile >> 2)]);
             if (blk < 0 || blk >= a.pool_blocks) blk = 0;
             const int64_t off = blk * a.block_stride + (int64_t)kvh * a.head_stride;
+            const int tb0 = (tile & 3) * kTile;
+            const int nrec = tile == nt_seq - 1 && nv_last < kTile
+                                 ? a.sz_off + (tb0 + nv_last) * 16 : a.block_bytes;
             const __amdgpu_buffer_rsrc_t rkt = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint8_t *>(a.kp + off), 0, a.block_bytes, kRsrcWord3);
+                const_cast<uint8_t *>(a.kp + off), 0, nrec, kRsrcWord3);
             const __amdgpu_buffer_rsrc_t rvt = __builtin_amdgcn_make_buffer_rsrc(
-                const_cast<uint8_t *>(a.vp + off), 0, a.block_bytes, kRsrcWord3);
-            issue_tile_at<BITS>(rkt, rvt, slot, 0u, (tile & 3) * kTile, lane, a.sz_off);
+                const_cast<uint8_t *>(a.vp + off), 0, nrec, kRsrcWord3);
+            issue_tile_at<BITS>(rkt, rvt, slot, 0u, tb0, lane, a.sz_off);
         } else {
             issue_tile<BITS>(rk, rv, slot, tile, lane, a.block_bytes, a.sz_off);
         }
     };
-    // the last tile of a ragged sequence: its missing tokens get scale/zero 0 in LDS (the
-    // bytes behind them may be anything) and are masked out of the softmax
-    const int nt_seq = (n_packed_b + kTile - 1) / kTile;
-    const int nv_last = n_packed_b - (nt_seq - 1) * kTile;
+    // An update that evicts: the wave that takes the tile holding the evicted token's new
+    // packed position quantizes that token (the old contents of the window slot, staged in
+    // sm.ev) exactly as kvq_append_evict does, writes it into its tile in LDS over whatever
+    // the pool held there, stores it into the pool, and only then writes the new token into
+    // the window slot. No other workgroup of the launch reads those pool bytes, and readers
+    // of the slot take the new token from k_new / v_new.
+    const int ev_tile = ev_pos >> 5;
+    const bool ev_mine = PAGED && ev_pos >= 0 && ev_pos < n_packed_b && ev_tile >= tlo &&
+                         ev_tile < thi && (ev_tile - tlo) % kWaves == wave;
+    bool ev_mapped = false;
+    // quantize the staged token (lanes 0..15 K, 16..31 V, one octet each), keep its bytes for
+    // the tile in sm.evc / sm.evs, store it into the pool, then write the new token into the
+    // window slot (run once, once the staging load is in)
+    auto evict_token = [&]() {
+        if constexpr (PAGED) {
+            const int oct = lane & 15;
+            const int is_v = (lane >> 4) & 1;
+            const u32x4 raw = *reinterpret_cast<const u32x4 *>(&sm.ev[is_v][8 * oct]);
+            uint32_t packed;
+            uint16_t sq, zq;
+            int flag;
+            if (a.hybrid) quantize_octet<BITS, true>(raw, packed, sq, zq, flag);
+            else quantize_octet<BITS, false>(raw, packed, sq, zq, flag);
+            PoolGeom g{const_cast<uint8_t *>(is_v ? a.vp : a.kp), a.pool_blocks, a.block_stride,
+                       a.head_stride, tbl, a.max_blocks, a.sz_off, a.flag_off};
+            uint8_t *blk = block_of(g, b, kvh, ev_pos);
+            if (lane < 32) {
+                sm.evc[is_v][oct] = packed;
+                if ((oct & 3) == 0) sm.evs[is_v][oct >> 2] = (uint32_t)sq | ((uint32_t)zq << 16);
+                if (blk) {
+                    if (a.hybrid) store_octet<BITS, true>(blk, g, ev_pos & 127, oct, packed, sq, zq, flag);
+                    else store_octet<BITS, false>(blk, g, ev_pos & 127, oct, packed, sq, zq, flag);
+                }
+                uint16_t *win = const_cast<uint16_t *>(is_v ? a.vres : a.kres) +
+                                (row * a.res_cap + upd_slot) * kHeadDim + 8 * oct;
+                *reinterpret_cast<u32x4 *>(win) =
+                    *reinterpret_cast<const u32x4 *>(&sm.ev[2 + is_v][8 * oct]);
+            }
+            ev_mapped = blk != nullptr;
+            lds_fence();
+        }
+    };
+    // the kept bytes into token ev_pos % 32 of the tile in LDS (over whatever the pool held)
+    auto evict_patch = [&](uint8_t *slot) {
+        const int t = ev_pos & 31;
+        const int oct = lane & 15;
+        const int is_v = (lane >> 4) & 1;
+        if (lane < 32 && ev_mapped) {
+            const uint32_t packed = sm.evc[is_v][oct];
+            const int grp = oct >> 2, jq = oct & 3;
+            uint8_t *cb = slot + (is_v ? G::CB : 0);
+            if (!is_v && BITS == 4) {
+                // the transposed order of 4-bit K codes in LDS (issue_tile_at)
+                *reinterpret_cast<uint32_t *>(cb + (t >> 4) * 1024 + grp * 256 + (t & 15) * 16 +
+                                              jq * 4) = packed;
+            } else {
+                uint8_t *c = cb + t * G::TOKB + grp * (4 * BITS) + jq * BITS;
+                if (BITS == 4) {
+                    *reinterpret_cast<uint32_t *>(c) = packed;
+                } else if (BITS == 2) {
+                    *reinterpret_cast<uint16_t *>(c) = (uint16_t)packed;
+                } else {
+                    c[0] = (uint8_t)packed;
+                    c[1] = (uint8_t)(packed >> 8);
+                    c[2] = (uint8_t)(packed >> 16);
+                }
+            }
+            if (jq == 0)
+                *reinterpret_cast<uint32_t *>(slot + (is_v ? G::VSZ : G::KSZ) + t * 16 + grp * 4) =
+                    sm.evs[is_v][grp];
+        }
+    };
+    // the number of valid tokens of a tile once it is in LDS; the tile of an update's
+    // evicted token (the sequence's last packed token, so its last tile) is patched first
     auto tail_fix = [&](uint8_t *slot, int tile) -> int {
         if constexpr (PAGED) {
-            if (tile == nt_seq - 1 && nv_last < kTile) {
-                if (lane >= nv_last && lane < kTile) {
-                    *reinterpret_cast<u32x4 *>(slot + G::KSZ + lane * 16) = u32x4{0u, 0u, 0u, 0u};
-                    *reinterpret_cast<u32x4 *>(slot + G::VSZ + lane * 16) = u32x4{0u, 0u, 0u, 0u};
+            if (tile == nt_seq - 1) {
+                if (ev_mine) {
+                    evict_patch(slot);
+                    lds_fence();
                 }
-                lds_fence();
                 return nv_last;
             }
         }
@@ -733,6 +841,25 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
                 const_cast<float *>(a.qnorm + row * kHeadDim), 0, kHeadDim * 4, kRsrcWord3);
             dma(rn, reinterpret_cast<uint8_t *>(&sm.qn[0]), lane * 16, 16);
         }
+    }
+
+    // the evicted token's old window contents and the new token, staged before this wave's
+    // tiles are asked for: they are older than every tile load waited for, so no wait of
+    // their own (a plain load here would have to wait for every load in flight)
+    if (ev_mine && lane < 16) {
+        const int64_t wrow = (row * a.res_cap + upd_slot) * kHeadDim;
+        const __amdgpu_buffer_rsrc_t rek = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.kres + wrow), 0, kHeadDim * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rev = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vres + wrow), 0, kHeadDim * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rnk = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.knew + row * kHeadDim), 0, kHeadDim * 2, kRsrcWord3);
+        const __amdgpu_buffer_rsrc_t rnv = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<uint16_t *>(a.vnew + row * kHeadDim), 0, kHeadDim * 2, kRsrcWord3);
+        dma(rek, reinterpret_cast<uint8_t *>(&sm.ev[0][0]), lane * 16, 16);
+        dma(rev, reinterpret_cast<uint8_t *>(&sm.ev[1][0]), lane * 16, 16);
+        dma(rnk, reinterpret_cast<uint8_t *>(&sm.ev[2][0]), lane * 16, 16);
+        dma(rnv, reinterpret_cast<uint8_t *>(&sm.ev[3][0]), lane * 16, 16);
     }
 
     // ---- ask for this wave's first RING tiles ----
@@ -851,6 +978,7 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
     const int pstride = 4 * kTile;
     if (nt_w > 0) {
         wait_behind<BITS>(nt_w - 1 < RING - 1 ? nt_w - 1 : RING - 1);
+        if (ev_mine) evict_token();      // its staging load is older than the tile just waited for
         PV cur;
         float alpha;
         bool resc;
@@ -919,10 +1047,12 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
         // from k_new / v_new here, and the workgroup of the row's first query heads (first
         // chunk of the launch that starts at head 0) stores it into the window; every
         // reader of that slot in these launches reads k_new / v_new instead
-        const int new_slot = a.knew ? n_res_b - 1 : -1;
+        // (a paged update places the new token at upd_slot; when it evicts, the slot is
+        // written by the wave that moves the old token out, after reading it)
+        const int new_slot = (PAGED && a.upd) ? upd_slot : (a.knew ? n_res_b - 1 : -1);
         const uint16_t *kn = a.knew ? a.knew + row * kHeadDim : kr;
         const uint16_t *vn = a.vnew ? a.vnew + row * kHeadDim : vr;
-        if (new_slot >= 0 && a.head_base == 0 && blockIdx.z == 0 && threadIdx.x < 32) {
+        if (new_slot >= 0 && ev_pos < 0 && a.head_base == 0 && blockIdx.z == 0 && threadIdx.x < 32) {
             const bool is_v = threadIdx.x >= 16;
             const int t = threadIdx.x & 15;
             uint16_t *dst = const_cast<uint16_t *>(is_v ? vr : kr) + (int64_t)new_slot * kHeadDim + 8 * t;

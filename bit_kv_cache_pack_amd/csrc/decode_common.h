@@ -38,6 +38,11 @@ struct DecArgs {
     int32_t max_blocks;
     int64_t pool_blocks, block_stride, head_stride;
     const int32_t *state;
+    // the update folded into a paged decode (DecodeParams::upd): state is read, the new
+    // state goes to state_out; hybrid / flag_off describe the blocks the evicted token
+    // is written into
+    int32_t upd, n_sink, hybrid, flag_off;
+    int32_t *state_out;
     // split merge inside the launch: the output [B][Hq][128] (fp32, or fp16 when out_f16),
     // the workspace of record slots, the slots per group, and the number of head chunks per
     // row (groups are (row, chunk))
@@ -46,6 +51,14 @@ struct DecArgs {
     void *ws;
     int32_t rec_per_group, n_chunks;
 };
+
+// The lane index, counted from the exec mask (valid where all 64 lanes are active, as in
+// the merge code after a workgroup barrier): a computation of its own, so the compiler does
+// not keep threadIdx.x & 63 in a register from the start of the kernel to its end.
+__device__ __forceinline__ int lane_full()
+{
+    return (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
 
 __device__ __forceinline__ void lds_fence()
 {
@@ -247,24 +260,23 @@ __device__ __forceinline__ uint32_t v_octet(const uint8_t *vcodes, int t, int j)
     return __builtin_amdgcn_alignbit(d[1], d[0], (byte & 3u) * 8);
 }
 
-// fp16 pair {hi(p0 * s0), hi(p1 * s1)}: each product rounded once to fp16 (v_fma_mix with
-// the fp16 scale taken from the low half of a {scale, zero} dword)
+// fp16 pair {hi(p0 * s0), hi(p1 * s1)}: each product of the fp32 p and the fp16 scale
+// (the low half of a {scale, zero} dword) formed in fp32 and rounded to fp16; the compiler
+// emits one v_fma_mix per half. (Written in C, not inline asm, so that the compiler sees
+// these VALU writes and keeps the wait states the MFMA that reads them needs.)
 __device__ __forceinline__ uint32_t pv_hi(float p0, uint32_t s0, float p1, uint32_t s1)
 {
-    uint32_t d;
-    asm("v_fma_mixlo_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "=v"(d) : "v"(p0), "v"(s0));
-    asm("v_fma_mixhi_f16 %0, %1, %2, 0 op_sel_hi:[0,1,0]" : "+v"(d) : "v"(p1), "v"(s1));
-    return d;
+    const _Float16 a = (_Float16)__builtin_fmaf(p0, (float)as_h2(s0)[0], 0.0f);
+    const _Float16 b = (_Float16)__builtin_fmaf(p1, (float)as_h2(s1)[0], 0.0f);
+    return h2_bits(half2_t{a, b});
 }
-// the fp16 of the remainders p0 * s0 - hi0 and p1 * s1 - hi1 (one rounding each)
+// the fp16 of the remainders p0 * s0 - hi0 and p1 * s1 - hi1 (one fused multiply-add each)
 __device__ __forceinline__ uint32_t pv_lo(float p0, uint32_t s0, float p1, uint32_t s1, uint32_t hi)
 {
-    uint32_t d;
-    asm("v_fma_mixlo_f16 %0, %1, %2, -%3 op_sel:[0,0,0] op_sel_hi:[0,1,1]"
-        : "=v"(d) : "v"(p0), "v"(s0), "v"(hi));
-    asm("v_fma_mixhi_f16 %0, %1, %2, -%3 op_sel:[0,0,1] op_sel_hi:[0,1,1]"
-        : "+v"(d) : "v"(p1), "v"(s1), "v"(hi));
-    return d;
+    const half2_t h = as_h2(hi);
+    const _Float16 a = (_Float16)__builtin_fmaf(p0, (float)as_h2(s0)[0], -(float)h[0]);
+    const _Float16 b = (_Float16)__builtin_fmaf(p1, (float)as_h2(s1)[0], -(float)h[1]);
+    return h2_bits(half2_t{a, b});
 }
 
 // kernel arguments from the validated call arguments (host)
@@ -300,6 +312,11 @@ inline DecArgs make_dec_args(const DecodeParams &p)
     a.block_stride = p.block_stride;
     a.head_stride = p.head_stride;
     a.state = p.state;
+    a.upd = p.upd;
+    a.n_sink = p.n_sink;
+    a.hybrid = p.hybrid;
+    a.flag_off = p.flag_off;
+    a.state_out = p.state_out;
     a.row_bytes = (int32_t)((int64_t)(p.n_packed / kBlockTokens) * p.block_bytes);
     a.out = p.out;
     a.out_f16 = p.out_f16;

@@ -33,6 +33,7 @@ hipError_t launch_append(const uint16_t *, const uint16_t *, uint16_t *, uint16_
 hipError_t launch_pack_tokens_paged(const PagedPool &, const uint16_t *, int32_t, int32_t, int64_t,
                                     int64_t, const int32_t *, const int32_t *, int32_t, uint8_t *,
                                     hipStream_t) { return none(); }
+hipError_t launch_copy_state(int32_t *, const int32_t *, int32_t, hipStream_t) { return none(); }
 hipError_t launch_append_evict(const PagedPool &, const uint16_t *, const uint16_t *, uint16_t *,
                                uint16_t *, int32_t, int32_t, uint8_t *, uint8_t *, int32_t *,
                                int32_t, int32_t, hipStream_t) { return none(); }

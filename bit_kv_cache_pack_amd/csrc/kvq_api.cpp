@@ -521,6 +521,13 @@ kvq_status kvq_append_evict(const kvq_format *fmt, const void *k_new, const void
 
 namespace {
 
+// the step's cache update folded into a paged decode (kvq_decode_attention_paged_append)
+struct PagedUpdate {
+    const void *k_new = nullptr, *v_new = nullptr;
+    int32_t n_sink = 0;
+    kvq_seq_state *state_out = nullptr;
+};
+
 kvq_status paged_common(const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq,
                         int32_t Hkv, const void *k_pool, const void *v_pool, int64_t pool_blocks,
                         int64_t block_stride_bytes, int64_t head_stride_bytes,
@@ -528,7 +535,7 @@ kvq_status paged_common(const kvq_format *fmt, const void *q_fp16, int32_t B, in
                         const kvq_seq_state *state, const void *k_res_fp16,
                         const void *v_res_fp16, int32_t res_capacity, const float *key_norm,
                         float sm_scale, int32_t num_splits, const DecodeSink &sink,
-                        hipStream_t stream)
+                        hipStream_t stream, const PagedUpdate *upd = nullptr)
 {
     kvq_status st = check_format(fmt);
     if (st != KVQ_OK) return st;
@@ -549,6 +556,18 @@ kvq_status paged_common(const kvq_format *fmt, const void *q_fp16, int32_t B, in
     st = check_pool(fmt, Hkv, pool_blocks, block_stride_bytes, head_stride_bytes, block_table,
                     max_blocks, pp);
     if (st != KVQ_OK) return st;
+    if (upd) {
+        if (!upd->k_new || !upd->v_new || !upd->state_out) return KVQ_ERR_NULL;
+        if (upd->n_sink < 0 || upd->n_sink >= res_capacity) return KVQ_ERR_SHAPE;
+        if (!aligned64(upd->k_new) || !aligned64(upd->v_new) || !aligned64(upd->state_out))
+            return KVQ_ERR_ALIGN;
+        // the launch reads state while it writes state_out
+        const uintptr_t a0 = reinterpret_cast<uintptr_t>(state);
+        const uintptr_t b0 = reinterpret_cast<uintptr_t>(upd->state_out);
+        const uintptr_t n = (uintptr_t)B * sizeof(kvq_seq_state);
+        if (a0 < b0 + n && b0 < a0 + n) return KVQ_ERR_SHAPE;
+        if (sink.fused) return KVQ_ERR_UNSUPPORTED;
+    }
     kvq::DecodeParams p{};
     p.qnorm = key_norm;
     p.q = static_cast<const uint16_t *>(q_fp16);
@@ -572,6 +591,30 @@ kvq_status paged_common(const kvq_format *fmt, const void *q_fp16, int32_t B, in
     p.block_stride = block_stride_bytes;
     p.head_stride = head_stride_bytes;
     p.state = reinterpret_cast<const int32_t *>(state);
+    if (upd && Hq / Hkv > 4) {
+        // more than one head chunk per kv-head row: the update as its own launch on a copy
+        // of the state, then the decode (the same result as the folded path)
+        int32_t *so = reinterpret_cast<int32_t *>(upd->state_out);
+        if (kvq::launch_copy_state(so, reinterpret_cast<const int32_t *>(state), B, stream) !=
+            hipSuccess)
+            return KVQ_ERR_LAUNCH;
+        const hipError_t e = kvq::launch_append_evict(
+            pp, static_cast<const uint16_t *>(upd->k_new), static_cast<const uint16_t *>(upd->v_new),
+            const_cast<uint16_t *>(p.kres), const_cast<uint16_t *>(p.vres), res_capacity,
+            upd->n_sink, const_cast<uint8_t *>(p.kp), const_cast<uint8_t *>(p.vp), so, B, Hkv, stream);
+        if (e != hipSuccess) return KVQ_ERR_LAUNCH;
+        p.state = so;
+        return launched(kvq::launch_decode_paged(p, stream));
+    }
+    if (upd) {
+        p.upd = 1;
+        p.knew = static_cast<const uint16_t *>(upd->k_new);
+        p.vnew = static_cast<const uint16_t *>(upd->v_new);
+        p.n_sink = upd->n_sink;
+        p.hybrid = fmt->hybrid;
+        p.flag_off = pp.flag_off;
+        p.state_out = reinterpret_cast<int32_t *>(upd->state_out);
+    }
     return launched(sink.fused ? kvq::launch_decode_paged_fused(p, stream)
                                : kvq::launch_decode_paged(p, stream));
 }
@@ -594,6 +637,25 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
                         head_stride_bytes, block_table, max_blocks, state, k_res_fp16, v_res_fp16,
                         res_capacity, key_norm, sm_scale, num_splits, partials(part_o, part_lse),
                         stream);
+}
+
+kvq_status kvq_decode_attention_paged_append(
+    const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv, void *k_pool,
+    void *v_pool, int64_t pool_blocks, int64_t block_stride_bytes, int64_t head_stride_bytes,
+    const int32_t *block_table, int32_t max_blocks, const kvq_seq_state *state,
+    kvq_seq_state *state_out, void *k_res_fp16, void *v_res_fp16, int32_t res_capacity,
+    int32_t n_sink, const void *k_new, const void *v_new, const float *key_norm, float sm_scale,
+    int32_t num_splits, float *part_o, float *part_lse, hipStream_t stream)
+{
+    PagedUpdate u;
+    u.k_new = k_new;
+    u.v_new = v_new;
+    u.n_sink = n_sink;
+    u.state_out = state_out;
+    return paged_common(fmt, q_fp16, B, Hq, Hkv, k_pool, v_pool, pool_blocks, block_stride_bytes,
+                        head_stride_bytes, block_table, max_blocks, state, k_res_fp16, v_res_fp16,
+                        res_capacity, key_norm, sm_scale, num_splits, partials(part_o, part_lse),
+                        stream, &u);
 }
 
 kvq_status kvq_decode_attention_paged_fused(const kvq_format *fmt, const void *q_fp16, int32_t B,

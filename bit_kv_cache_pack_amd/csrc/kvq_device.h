@@ -26,18 +26,23 @@ __device__ __forceinline__ float dpp_f(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
 }
 
-// max over the 16 lanes of a row; every lane of the row gets the result. Each step is one
-// v_max_f32 with a DPP source (the s_nop covers the gfx9 hazard of a DPP read of a VGPR
-// written by the previous VALU instruction).
-#define KVQ_DPP_MAX(v, CTRL)                                                              \
-    asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 " CTRL " row_mask:0xf bank_mask:0xf"       \
-        : "=v"(v) : "v"(v))
+// max over the 16 lanes of a row (finite values or -inf); every lane of the row gets the
+// result. Each step is a DPP move and v_med3_f32 against FLT_MAX: the median of
+// {a, b, FLT_MAX} is max(a, b). Built from compiler intrinsics rather than inline asm, so
+// that the compiler sees every VGPR write and inserts the wait states that DPP and MFMA
+// neighbours need.
+template <int CTRL>
+__device__ __forceinline__ float dpp_bc(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xF, 0xF, true));
+}
 __device__ __forceinline__ float row_max16(float v)
 {
-    KVQ_DPP_MAX(v, "row_ror:8");
-    KVQ_DPP_MAX(v, "row_ror:4");
-    KVQ_DPP_MAX(v, "quad_perm:[2,3,0,1]");
-    KVQ_DPP_MAX(v, "quad_perm:[1,0,3,2]");
+    constexpr float kBig = 3.402823466e38f;
+    v = __builtin_amdgcn_fmed3f(v, dpp_bc<0x128>(v), kBig);
+    v = __builtin_amdgcn_fmed3f(v, dpp_bc<0x124>(v), kBig);
+    v = __builtin_amdgcn_fmed3f(v, dpp_bc<0x4E>(v), kBig);
+    v = __builtin_amdgcn_fmed3f(v, dpp_bc<0xB1>(v), kBig);
     return v;
 }
 // sum over the 16 lanes of a row; every lane of the row gets the result
@@ -66,9 +71,8 @@ __device__ __forceinline__ uint32_t h2_bits(half2_t h) { return __builtin_bit_ca
 // operand, so keeping `base` in a VGPR lets the compiler fuse it into one v_and_or_b32.
 __device__ __forceinline__ uint32_t vconst(uint32_t c)
 {
-    uint32_t v;
-    asm("v_mov_b32 %0, %1" : "=v"(v) : "n"(c));
-    return v;
+    // an identity DPP move: a VALU op the compiler cannot fold back into a literal
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)c, 0xE4, 0xF, 0xF, false);
 }
 
 // fp16 magic-number conversion of small integer codes: OR-ing a code into the mantissa of

@@ -38,6 +38,12 @@ struct DecodeParams {
     void *out;
     int32_t out_f16;
     void *ws;
+    // paged only: the step's cache update (kvq_append_evict) folded into the decode: the
+    // new token (knew / vnew) enters the window as that call places it, the evicted token
+    // (if any) is quantized into the pool, state is only read and the updated state is
+    // written to state_out
+    int32_t upd, n_sink, hybrid, flag_off;
+    int32_t *state_out;
 };
 
 // Workspace of the fused split merge: per group (a row's chunk of up to 4 query heads) one
@@ -99,6 +105,9 @@ hipError_t launch_pack_tokens_paged(const PagedPool &pool, const uint16_t *src, 
                                     int32_t Hkv, int64_t src_row_stride, int64_t src_tok_stride,
                                     const int32_t *count, const int32_t *start, int32_t max_count,
                                     uint8_t *dst_pool, hipStream_t stream);
+
+// copy of B sequence states (4 int32 each), stream-ordered
+hipError_t launch_copy_state(int32_t *dst, const int32_t *src, int32_t B, hipStream_t stream);
 
 hipError_t launch_append_evict(const PagedPool &pool, const uint16_t *k_new,
                                const uint16_t *v_new, uint16_t *k_res, uint16_t *v_res,

@@ -32,7 +32,8 @@ EXPORTED = ("kvq_quantize_pack", "kvq_decode_attention", "kvq_decode_attention_k
             "kvq_append_evict", "kvq_decode_attention_paged", "kvq_quantize_pack_outer",
             "kvq_decode_attention_outer", "kvq_decode_attention_append",
             "kvq_decode_attention_fused", "kvq_decode_attention_paged_fused",
-            "kvq_decode_attention_fused_noalloc", "kvq_stream_read")
+            "kvq_decode_attention_fused_noalloc", "kvq_stream_read",
+            "kvq_decode_attention_paged_append")
 # exported calls that return a size rather than a status
 EXPORTED_SIZE = ("kvq_decode_workspace_bytes",)
 
@@ -134,6 +135,9 @@ def lib():
         L.kvq_decode_attention_paged.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64, i64,
                                                  vp, i32, vp, vp, vp, i32, vp, f32, i32, vp, vp,
                                                  vp]
+        L.kvq_decode_attention_paged_append.argtypes = [fp, vp, i32, i32, i32, vp, vp, i64, i64,
+                                                        i64, vp, i32, vp, vp, vp, vp, i32, i32,
+                                                        vp, vp, vp, f32, i32, vp, vp, vp]
         L.kvq_decode_attention_fused.argtypes = [fp, vp, vp, i32, i32, i32, vp, vp, i64, i32,
                                                  vp, vp, i32, i32, vp, vp, f32, i32, vp, i64,
                                                  vp, i32, vp]
@@ -351,6 +355,23 @@ def kvq_decode_attention_paged(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k
                                           num_splits, _ptr(part_o), _ptr(part_lse),
                                           _stream(stream, q_fp16))
     _check("kvq_decode_attention_paged", st)
+
+
+def kvq_decode_attention_paged_append(fmt: Format, q_fp16, B: int, Hq: int, Hkv: int, k_pool,
+                                      v_pool, pool_blocks: int, block_stride_bytes: int,
+                                      head_stride_bytes: int, block_table, max_blocks: int,
+                                      state, state_out, k_res_fp16, v_res_fp16,
+                                      res_capacity: int, n_sink: int, k_new, v_new,
+                                      sm_scale: float, num_splits: int, part_o, part_lse,
+                                      stream=None, key_norm=None):
+    f = fmt.c()
+    st = lib().kvq_decode_attention_paged_append(
+        C.byref(f), _ptr(q_fp16), B, Hq, Hkv, _ptr(k_pool), _ptr(v_pool), pool_blocks,
+        block_stride_bytes, head_stride_bytes, _ptr(block_table), max_blocks, _ptr(state),
+        _ptr(state_out), _ptr(k_res_fp16), _ptr(v_res_fp16), res_capacity, n_sink, _ptr(k_new),
+        _ptr(v_new), _ptr(key_norm), float(sm_scale), num_splits, _ptr(part_o), _ptr(part_lse),
+        _stream(stream, q_fp16))
+    _check("kvq_decode_attention_paged_append", st)
 
 
 def kvq_decode_workspace_bytes(B: int, Hq: int, Hkv: int, num_splits: int) -> int:

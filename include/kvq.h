@@ -597,6 +597,29 @@ kvq_status kvq_decode_attention_paged(const kvq_format *fmt, const void *q_fp16,
                                       float *part_o, float *part_lse, hipStream_t stream);
 
 /*
+ * kvq_decode_attention_paged_append -- one serving step of the paged cache in one call:
+ * kvq_append_evict (the new token enters the window; when the window is full the token in
+ * slot next_slot is quantized into packed position n_packed and the new token takes its
+ * slot; [InnerQ] sec. 2.3) followed by kvq_decode_attention_paged over the updated cache,
+ * with the same windows, pool bytes, state and partials as those two calls, bit for bit.
+ * The update is applied inside the decode launch: `state` is only read, the updated state
+ * is written to `state_out` (the caller alternates the two buffers from step to step).
+ * With more than four query heads per kv-head the two calls run as two launches
+ * internally (same results).
+ *   state, state_out  [B] states, 64-byte aligned, not overlapping
+ *   n_sink, k_new, v_new   as kvq_append_evict; k_res_fp16 / v_res_fp16 and the pools are
+ *                   written (the new token and the evicted token)
+ *   Other arguments, outputs and limits: as kvq_decode_attention_paged.
+ */
+kvq_status kvq_decode_attention_paged_append(
+    const kvq_format *fmt, const void *q_fp16, int32_t B, int32_t Hq, int32_t Hkv, void *k_pool,
+    void *v_pool, int64_t pool_blocks, int64_t block_stride_bytes, int64_t head_stride_bytes,
+    const int32_t *block_table, int32_t max_blocks, const kvq_seq_state *state,
+    kvq_seq_state *state_out, void *k_res_fp16, void *v_res_fp16, int32_t res_capacity,
+    int32_t n_sink, const void *k_new, const void *v_new, const float *key_norm, float sm_scale,
+    int32_t num_splits, float *part_o, float *part_lse, hipStream_t stream);
+
+/*
  * kvq_decode_attention_paged_fused -- kvq_decode_attention_paged with the split merge in
  * the same launch, as kvq_decode_attention_fused: the output [B][Hq][head_dim] (out_dtype
  * as kvq_combine), the workspace as for kvq_decode_attention_fused. A sequence that attends

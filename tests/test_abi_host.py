@@ -402,6 +402,34 @@ def test_decode_paged_rejects(kw, status):
     assert _dp(**kw) == status
 
 
+def _dpa(fmt=None, q=A, B=2, Hq=8, Hkv=2, kp=A, vp=A, state=A, state_out=A + 4096, kr=A, vr=A,
+         cap=128, sink=4, knew=A, vnew=A, kn=None, sm=0.088, S=4, po=A, pl=A, **kw):
+    f = _fmt() if fmt is None else fmt
+    p = _pool_kw(**kw)
+    return K.lib().kvq_decode_attention_paged_append(
+        C.byref(f), q, B, Hq, Hkv, kp, vp, p["pool_blocks"], p["bs"], p["hs"], p["tbl"],
+        p["maxb"], state, state_out, kr, vr, cap, sink, knew, vnew, kn, sm, S, po, pl, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(knew=None), K.KVQ_ERR_NULL),
+    (dict(vnew=None), K.KVQ_ERR_NULL),
+    (dict(state_out=None), K.KVQ_ERR_NULL),
+    (dict(state=None), K.KVQ_ERR_NULL),
+    (dict(sink=-1), K.KVQ_ERR_SHAPE),
+    (dict(sink=128), K.KVQ_ERR_SHAPE),
+    (dict(state_out=A), K.KVQ_ERR_SHAPE),                 # the same buffer
+    (dict(state_out=A + 64, B=5), K.KVQ_ERR_SHAPE),      # overlapping (5 states = 80 bytes)
+    (dict(state_out=A + 4096 + 16), K.KVQ_ERR_ALIGN),
+    (dict(knew=A + 8), K.KVQ_ERR_ALIGN),
+    (dict(S=0), K.KVQ_ERR_SHAPE),
+    (dict(Hq=34, Hkv=2), K.KVQ_ERR_UNSUPPORTED),
+    (dict(tbl=None), K.KVQ_ERR_NULL),
+])
+def test_decode_paged_append_rejects(kw, status):
+    assert _dpa(**kw) == status
+
+
 def test_suggest_splits_paged_bounds():
     assert K.suggest_splits_paged(0, 0, 8) == 1
     # 16 sequences of 1.5K..32K tokens, 8 kv heads: 16 splits

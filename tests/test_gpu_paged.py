@@ -495,3 +495,66 @@ def test_serving_run_with_key_normalization(oracle_mod):
     assert np.array_equal(dk.cpu().numpy(), okp) and np.array_equal(dv.cpu().numpy(), ovp)
     assert np.array_equal(dkr.cpu().numpy().view(np.uint16), okr.view(np.uint16))
     assert_close(out.cpu().numpy(), ref, "serving run with key normalization")
+
+
+@pytest.mark.parametrize("bits,hybrid,Hq,Hkv,cap,n_sink,steps,S_,layout", [
+    (4, False, 8, 2, 16, 4, 40, 3, "block_major"),     # gq 4: the update inside the decode
+    (4, False, 32, 8, 8, 0, 30, 16, "head_major"),
+    (2, True, 4, 4, 8, 2, 30, 2, "block_major"),       # gq 1
+    (3, False, 6, 2, 16, 3, 25, 1, "block_major"),     # gq 3, one split
+    (3, True, 16, 2, 8, 1, 20, 4, "head_major"),       # gq 8: two launches inside the call
+])
+def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hkv, cap, n_sink,
+                                                steps, S_, layout):
+    """kvq_decode_attention_paged_append equals kvq_append_evict followed by
+    kvq_decode_attention_paged, step after step: windows, pools, states and partials bit
+    for bit (sequences that start with an empty window, a full one, a partly filled one, and
+    packed lengths that put the evicted token at every position of a tile and of a block);
+    the final output also against the oracle."""
+    from gpu_common import DEV, assert_close
+    O = oracle_mod
+    rng = np.random.default_rng(bits * 100 + Hq + cap)
+    fmt, ofmt = K.Format(bits, 128, hybrid), O.Format(bits, 128, hybrid)
+    B = 4
+    n_packed = [0, 77, 127, 31]
+    n_res = [0, cap, min(3, cap - 1), cap]
+    nxt = [n_sink, n_sink + (5 % (cap - n_sink)), n_sink, cap - 1]
+    c = _paged_case(O, rng, fmt, ofmt, B, Hq, Hkv, [n + steps + 1 for n in n_packed], n_res, cap,
+                    layout)
+    # the pools hold n_packed[b] + steps + 1 tokens per sequence; the state says n_packed[b]
+    st0 = _state([[n_packed[b], n_res[b], nxt[b], 7] for b in range(B)])
+    mb = c["tbl"].shape[1]
+    print(f"[paged append] bits={bits} hybrid={hybrid} Hq={Hq} Hkv={Hkv} cap={cap} "
+          f"sink={n_sink} S={S_} {layout}", flush=True)
+    dtbl = _dev(c["tbl"])
+    a = [_dev(c["kpool"]), _dev(c["vpool"]), _dev(c["kres"]), _dev(c["vres"]), _dev(st0)]
+    bb = [_dev(c["kpool"]), _dev(c["vpool"]), _dev(c["kres"]), _dev(c["vres"])]
+    s_in, s_out = _dev(st0), torch.full_like(_dev(st0), -1)
+    po_a = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=DEV)
+    pl_a = torch.empty((B, Hq, S_), dtype=torch.float32, device=DEV)
+    po_b, pl_b = torch.empty_like(po_a), torch.empty_like(pl_a)
+    for i in range(steps):
+        kn = _dev(_f16(rng.standard_normal((B, Hkv, 128)) * 2))
+        vn = _dev(_f16(rng.standard_normal((B, Hkv, 128))))
+        q = _dev(_f16(rng.standard_normal((B, Hq, 128))))
+        K.kvq_append_evict(fmt, kn, vn, a[2], a[3], cap, n_sink, a[0], a[1], c["npool"], c["bs"],
+                           c["hs"], dtbl, mb, a[4], B, Hkv)
+        K.kvq_decode_attention_paged(fmt, q, B, Hq, Hkv, a[0], a[1], c["npool"], c["bs"], c["hs"],
+                                     dtbl, mb, a[4], a[2], a[3], cap, SM, S_, po_a, pl_a)
+        K.kvq_decode_attention_paged_append(fmt, q, B, Hq, Hkv, bb[0], bb[1], c["npool"], c["bs"],
+                                            c["hs"], dtbl, mb, s_in, s_out, bb[2], bb[3], cap,
+                                            n_sink, kn, vn, SM, S_, po_b, pl_b)
+        torch.cuda.synchronize()
+        assert torch.equal(a[4], s_out), f"state, step {i}"
+        assert torch.equal(pl_a, pl_b), f"lse, step {i}"
+        assert torch.equal(po_a, po_b), f"partial outputs, step {i}"
+        for x, y, what in zip(a[:4], bb, ("K pool", "V pool", "K window", "V window")):
+            assert torch.equal(x, y), f"{what}, step {i}"
+        s_in, s_out = s_out, s_in
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
+    K.kvq_combine(po_b, pl_b, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
+    torch.cuda.synchronize()
+    ref = O.attention_paged(ofmt, q.cpu().numpy(), Hkv, bb[0].cpu().numpy(),
+                            bb[1].cpu().numpy(), c["tbl"], s_in.cpu().numpy(), bb[2].cpu().numpy(),
+                            bb[3].cpu().numpy(), sm=SM, block_stride=c["bs"], head_stride=c["hs"])
+    assert_close(out.cpu().numpy(), ref, "attention after the last step")
