@@ -441,18 +441,28 @@ __device__ __forceinline__ void merge_waves(SM &sm, const WaveState &st, int wav
     v1 = 0.f;
     lse2 = -INFINITY;
     if (h < NH) {
+        // every wave's (m, l) and output pair read at once (one LDS round trip)
+        float mw[W], lw[W];
+        float2 ow[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) {
+            mw[w] = sm.ml[w][h][0];
+            lw[w] = sm.ml[w][h][1];
+            ow[w] = *reinterpret_cast<const float2 *>(sm.mo(w) + h * kHeadDim + d);
+        }
         float Mx = -INFINITY;
 #pragma unroll
-        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, sm.ml[w][h][0]);
+        for (int w = 0; w < W; ++w) Mx = fmaxf(Mx, mw[w]);
+        // no branch (so the loads above are not moved behind one): with no attended token
+        // in the workgroup every e is exp2(-inf) = 0 and L, o0, o1 stay 0
+        const float Mref = Mx == -INFINITY ? 0.0f : Mx;
         float o0 = 0.f, o1 = 0.f, L = 0.f;
-        if (Mx != -INFINITY) {
 #pragma unroll
-            for (int w = 0; w < W; ++w) {
-                const float e = __builtin_amdgcn_exp2f(sm.ml[w][h][0] - Mx);
-                L += e * sm.ml[w][h][1];
-                o0 += e * sm.mo(w)[h * kHeadDim + d];
-                o1 += e * sm.mo(w)[h * kHeadDim + d + 1];
-            }
+        for (int w = 0; w < W; ++w) {
+            const float e = __builtin_amdgcn_exp2f(mw[w] - Mref);
+            L += e * lw[w];
+            o0 += e * ow[w].x;
+            o1 += e * ow[w].y;
         }
         if (L > 0.f) {
             const float inv = 1.0f / L;

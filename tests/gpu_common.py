@@ -2,6 +2,8 @@
 HIP path through the C ABI binding (no computation here)."""
 from __future__ import annotations
 
+import os
+
 import numpy as np
 import torch
 
@@ -56,6 +58,8 @@ def errors(got, ref) -> tuple[float, float]:
 
 def assert_close(got, ref, what=""):
     ma, rl = errors(got, ref)
+    if os.environ.get("KVQ_REPORT_ERRORS"):
+        print(f"[errors] {what}: max_abs={ma:.3e} rel_l2={rl:.3e}", flush=True)
     assert ma <= TOL_MAX_ABS and rl <= TOL_REL_L2, f"{what}: max_abs={ma:.3e} rel_l2={rl:.3e}"
     return ma, rl
 
