@@ -49,11 +49,9 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(QPArgs a)
     const int g = oct >> 2;            // group 0..3
     const int j = oct & 3;             // octet within the group
 
-    __shared__ uint32_t flags[16];
-    if (HYBRID) {
-        if (threadIdx.x < 16) flags[threadIdx.x] = 0;
-        __syncthreads();
-    }
+    // hybrid mode flags of this wave's 32 tokens: bits wave*128 .. wave*128+127 of the
+    // block's 512 (bit = token * 4 + group), gathered from wave ballots, no LDS
+    uint32_t fw[4] = {0u, 0u, 0u, 0u};
 
     const uint16_t *src = a.src + row * a.src_row_stride + (int64_t)blk * kBlockTokens * a.src_tok_stride;
     uint8_t *dblk = a.dst + row * a.dst_row_stride + (int64_t)(a.first_block + blk) * a.block_bytes;
@@ -84,19 +82,23 @@ __global__ __launch_bounds__(256) void quant_pack_kernel(QPArgs a)
             gptr[1] = (uint8_t)(packed >> 8);
             gptr[2] = (uint8_t)(packed >> 16);
         }
-        if (j == 0) {
+        if (j == 0)
             *reinterpret_cast<uint32_t *>(dblk + a.sz_off + (tb * kGroups + g) * 4) =
                 (uint32_t)out_s | ((uint32_t)out_z << 16);
-            if (HYBRID && flag) {
-                const int bit = tb * kGroups + g;
-                atomicOr(&flags[bit >> 5], 1u << (bit & 31));
-            }
+        if (HYBRID) {
+            // lane 16 tl + 4 g holds the flag of token tl, group g of this step: its bit is
+            // it * 16 + tl * 4 + g of the wave's range
+            const uint64_t m = __builtin_amdgcn_ballot_w64(j == 0 && flag);
+            uint32_t b16 = 0;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) b16 |= (uint32_t)((m >> (16 * (k >> 2) + 4 * (k & 3))) & 1u) << k;
+            fw[it >> 1] |= b16 << (16 * (it & 1));
         }
     }
     if (HYBRID) {
-        __syncthreads();
-        if (threadIdx.x < 16)
-            reinterpret_cast<uint32_t *>(dblk + a.flag_off)[threadIdx.x] = flags[threadIdx.x];
+        if (lane < 4)
+            reinterpret_cast<uint32_t *>(dblk + a.flag_off)[wave * 4 + lane] =
+                lane == 0 ? fw[0] : lane == 1 ? fw[1] : lane == 2 ? fw[2] : fw[3];
     }
 }
 
