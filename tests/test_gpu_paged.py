@@ -497,15 +497,17 @@ def test_serving_run_with_key_normalization(oracle_mod):
     assert_close(out.cpu().numpy(), ref, "serving run with key normalization")
 
 
-@pytest.mark.parametrize("bits,hybrid,Hq,Hkv,cap,n_sink,steps,S_,layout", [
-    (4, False, 8, 2, 16, 4, 40, 3, "block_major"),     # gq 4: the update inside the decode
-    (4, False, 32, 8, 8, 0, 30, 16, "head_major"),
-    (2, True, 4, 4, 8, 2, 30, 2, "block_major"),       # gq 1
-    (3, False, 6, 2, 16, 3, 25, 1, "block_major"),     # gq 3, one split
-    (3, True, 16, 2, 8, 1, 20, 4, "head_major"),       # gq 8: two launches inside the call
+@pytest.mark.parametrize("bits,hybrid,Hq,Hkv,cap,n_sink,steps,S_,layout,knorm", [
+    (4, False, 8, 2, 16, 4, 40, 3, "block_major", False),  # gq 4: the update inside the decode
+    (4, False, 32, 8, 8, 0, 30, 16, "head_major", False),
+    (2, True, 4, 4, 8, 2, 30, 2, "block_major", False),    # gq 1
+    (3, False, 6, 2, 16, 3, 25, 1, "block_major", False),  # gq 3, one split
+    (3, True, 16, 2, 8, 1, 20, 4, "head_major", False),    # gq 8: two launches inside the call
+    (4, False, 8, 2, 16, 4, 12, 3, "block_major", True),   # with key-channel factors
+    (2, True, 16, 2, 8, 0, 12, 2, "head_major", True),     # the same through two launches
 ])
 def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hkv, cap, n_sink,
-                                                steps, S_, layout):
+                                                steps, S_, layout, knorm):
     """kvq_decode_attention_paged_append equals kvq_append_evict followed by
     kvq_decode_attention_paged, step after step: windows, pools, states and partials bit
     for bit (sequences that start with an empty window, a full one, a partly filled one, and
@@ -533,6 +535,9 @@ def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hk
     po_a = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=DEV)
     pl_a = torch.empty((B, Hq, S_), dtype=torch.float32, device=DEV)
     po_b, pl_b = torch.empty_like(po_a), torch.empty_like(pl_a)
+    # key-channel factors [B * Hkv][128] (both calls scale q by them the same way)
+    norm = (rng.uniform(0.25, 4.0, (B * Hkv, 128)).astype(np.float32) if knorm else None)
+    dnorm = _dev(norm) if knorm else None
     for i in range(steps):
         kn = _dev(_f16(rng.standard_normal((B, Hkv, 128)) * 2))
         vn = _dev(_f16(rng.standard_normal((B, Hkv, 128))))
@@ -540,10 +545,11 @@ def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hk
         K.kvq_append_evict(fmt, kn, vn, a[2], a[3], cap, n_sink, a[0], a[1], c["npool"], c["bs"],
                            c["hs"], dtbl, mb, a[4], B, Hkv)
         K.kvq_decode_attention_paged(fmt, q, B, Hq, Hkv, a[0], a[1], c["npool"], c["bs"], c["hs"],
-                                     dtbl, mb, a[4], a[2], a[3], cap, SM, S_, po_a, pl_a)
+                                     dtbl, mb, a[4], a[2], a[3], cap, SM, S_, po_a, pl_a,
+                                     key_norm=dnorm)
         K.kvq_decode_attention_paged_append(fmt, q, B, Hq, Hkv, bb[0], bb[1], c["npool"], c["bs"],
                                             c["hs"], dtbl, mb, s_in, s_out, bb[2], bb[3], cap,
-                                            n_sink, kn, vn, SM, S_, po_b, pl_b)
+                                            n_sink, kn, vn, SM, S_, po_b, pl_b, key_norm=dnorm)
         torch.cuda.synchronize()
         assert torch.equal(a[4], s_out), f"state, step {i}"
         assert torch.equal(pl_a, pl_b), f"lse, step {i}"
@@ -554,7 +560,14 @@ def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hk
     out = torch.empty((B, Hq, 128), dtype=torch.float32, device=DEV)
     K.kvq_combine(po_b, pl_b, B, Hq, 128, S_, out, K.KVQ_OUT_F32)
     torch.cuda.synchronize()
-    ref = O.attention_paged(ofmt, q.cpu().numpy(), Hkv, bb[0].cpu().numpy(),
+    qh = q.cpu().numpy()
+    if knorm:
+        # q' = fp16(q * factor), the binary32 product rounded once to fp16, per channel of
+        # the head's kv-head row
+        gq = Hq // Hkv
+        f = norm.reshape(B, Hkv, 1, 128).repeat(gq, axis=2).reshape(B, Hq, 128)
+        qh = (qh.astype(np.float32) * f).astype(np.float16)
+    ref = O.attention_paged(ofmt, qh, Hkv, bb[0].cpu().numpy(),
                             bb[1].cpu().numpy(), c["tbl"], s_in.cpu().numpy(), bb[2].cpu().numpy(),
                             bb[3].cpu().numpy(), sm=SM, block_stride=c["bs"], head_stride=c["hs"])
     assert_close(out.cpu().numpy(), ref, "attention after the last step")
