@@ -209,9 +209,15 @@ def config_bench(name, args, K, S, dev, sptr, timed, cu):
 
     n = args.per_config_steps
     warm_clocks(dev)        # the GPU idled while the inputs were generated on the host
-    step_ms = timed(step, n, 20)
-    dec_ms = timed(decode, n, 5)
-    fused_ms = timed(fused, n, 5)
+    # three interleaved rounds, each loop behind its own warm-up; the median of the rounds
+    # (the clock drifts by a few percent over a long run)
+    import statistics
+    meas = {"step": [], "dec": [], "fused": []}
+    for _ in range(3):
+        meas["step"].append(timed(step, n, 100))
+        meas["dec"].append(timed(decode, n, 50))
+        meas["fused"].append(timed(fused, n, 50))
+    step_ms, dec_ms, fused_ms = (statistics.median(meas[k]) for k in ("step", "dec", "fused"))
     res = {"B": wl.B, "Hq": wl.Hq, "Hkv": wl.Hkv, "L": wl.L, "bits": wl.bits,
            "hybrid": wl.hybrid, "splits": S_, "cache_copies": copies,
            "algorithmic_bytes_per_step": step_bytes,
