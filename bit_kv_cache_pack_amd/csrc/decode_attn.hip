@@ -495,10 +495,11 @@ __device__ __forceinline__ void merge_store(SM &sm, const WaveState &st, int wav
 
 // ---------------------------------------------------------------------------------------
 // Split merge inside the decode launch (kvq_decode_attention_fused). The splits of one group
-// (a row's head chunk) form a tree of fan-in 8: every workgroup stores its record (the
-// output of the chunk's heads and their log-sum-exp), then counts itself in its parent's
-// counter; the last of a parent's (up to 8) children merges their records into the parent's
-// record and goes up one level, and the last one at the top writes the output. Nobody waits
+// (a row's head chunk) form a tree of fan-in 32 (one level up to 32 splits): every workgroup
+// stores its record (the output of the chunk's heads and their log-sum-exp), then counts
+// itself in its parent's counter; the last of a parent's (up to 32) children merges their
+// records into the parent's record and goes up one level, and the last one at the top
+// writes the output. Nobody waits
 // for anybody, so the launch drains however its workgroups are scheduled.
 // Records and counters are read and written with device-scope coherent accesses (the sc1
 // cache policy: the L2 of each XCD passes them through), and a workgroup counts itself only
@@ -548,11 +549,17 @@ __device__ __forceinline__ void rec_merge(__amdgpu_buffer_rsrc_t rr, int first, 
     uint32_t lb[kFanIn];
 #pragma unroll
     for (int j = 0; j < kFanIn; ++j) {
-        const int rec = first + (j < cnt ? j : 0);
-        x[j] = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
-                                                    0, kScDevice);
-        lb[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)((rec * kRecFloats + 4 * kHeadDim + h) * 4),
-                                                     0, kScDevice);
+        // (cnt is uniform: a node with fewer children issues only their loads)
+        if (j < cnt) {
+            const int rec = first + j;
+            x[j] = __builtin_amdgcn_raw_buffer_load_b64(rr, (uint32_t)((rec * kRecFloats + h * kHeadDim + d) * 4),
+                                                        0, kScDevice);
+            lb[j] = __builtin_amdgcn_raw_buffer_load_b32(rr, (uint32_t)((rec * kRecFloats + 4 * kHeadDim + h) * 4),
+                                                         0, kScDevice);
+        } else {
+            x[j] = u32x2{0u, 0u};
+            lb[j] = 0xff800000u;     // -inf: weighs nothing
+        }
     }
     float M = -INFINITY;
 #pragma unroll

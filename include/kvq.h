@@ -387,9 +387,9 @@ kvq_status kvq_combine(const float *part_o, const float *part_lse, int32_t B, in
  * kvq_decode_attention_append's new token) merged into the output inside the same launch,
  * by the log-sum-exp rule of kvq_combine ([BitDecoding] sec. 2.2-2.3 for the decode,
  * sec. 4.2 for the split-K merge). The splits of each (batch, kv-head, chunk of up to 4
- * query heads) merge in a tree of fan-in 8: every split stores its partial in the
- * workspace and counts itself in its parent's counter, and the last of a parent's children
- * merges them; no workgroup waits for another.
+ * query heads) merge in a tree of fan-in 32 (one level up to 32 splits): every split
+ * stores its partial in the workspace and counts itself in its parent's counter, and the
+ * last of a parent's children merges them; no workgroup waits for another.
  *   key_norm        NULL, or fp32 [B*Hkv][128] key-channel factors (as kvq_decode_attention_knorm)
  *   k_new_fp16, v_new_fp16  NULL (both), or the new token [B][Hkv][head_dim] that becomes
  *                   window slot n_res - 1, as in kvq_decode_attention_append (the windows are
@@ -431,7 +431,7 @@ kvq_status kvq_decode_attention_fused(const kvq_format *fmt, const void *q_fp16,
  *   Arguments, outputs, validation and limits: as kvq_decode_attention_fused without
  *   workspace / workspace_bytes; KVQ_ERR_TOO_LARGE when kvq_decode_workspace_bytes(B, Hq,
  *   Hkv, num_splits) exceeds KVQ_NOALLOC_SCRATCH_BYTES (e.g. 8 rows of 4 query heads take
- *   1.2 MB at 64 splits; 1024 splits need 19.5 MB and are rejected).
+ *   1.1 MB at 64 splits; 1024 splits need 17.6 MB and are rejected).
  *   Every call on one GPU shares that GPU's array: calls that may overlap on one GPU (other
  *   streams, other threads) race and give undefined results; serialize them, or use
  *   kvq_decode_attention_fused with separate workspaces.
@@ -452,7 +452,7 @@ kvq_status kvq_decode_attention_fused_noalloc(const kvq_format *fmt, const void 
  * kvq_decode_workspace_bytes -- bytes of workspace kvq_decode_attention_fused and
  * kvq_decode_attention_paged_fused need for these sizes (0 when num_splits == 1; -1 for
  * sizes those calls reject): per chunk of up to 4 query heads of every (batch, kv-head),
- * one 2080-byte slot per node below the root of the fan-in-8 split tree (the node's
+ * one 2080-byte slot per node below the root of the fan-in-32 split tree (the node's
  * partial: 4 x 128 fp32 outputs and 4 log-sum-exps; its padding word holds the counter of
  * the parent whose first child it is). Every call lays its slots out from the start of the
  * workspace on the same 2080-byte grid, which is why one zeroed workspace serves calls of

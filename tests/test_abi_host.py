@@ -506,12 +506,12 @@ def test_split_rule_on_the_workloads():
 
 def _ws_bytes(B, Hq, Hkv, S):
     """The header's workspace size: per (batch, kv-head, chunk of <= 4 query heads) one
-    2080-byte slot per node below the root of the fan-in-8 split tree."""
+    2080-byte slot per node below the root of the fan-in-32 split tree."""
     slots = 0
     n = S
     while n > 1:
         slots += n
-        n = (n + 7) // 8
+        n = (n + 31) // 32
     return B * Hkv * ((Hq // Hkv + 3) // 4) * slots * 2080
 
 
@@ -524,8 +524,9 @@ def test_decode_workspace_bytes(B, Hq, Hkv, S):
 
 def test_decode_workspace_bytes_known_values():
     assert K.kvq_decode_workspace_bytes(1, 32, 8, 1) == 0
-    # 8 rows x 1 chunk; S = 64: 64 + 8 slots
-    assert K.kvq_decode_workspace_bytes(1, 32, 8, 64) == 8 * 72 * 2080
+    # 8 rows x 1 chunk; S = 64: 64 + 2 slots; S = 32: 32 slots (one level)
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 64) == 8 * 66 * 2080
+    assert K.kvq_decode_workspace_bytes(1, 32, 8, 32) == 8 * 32 * 2080
     for bad in [(0, 8, 2, 4), (1, 8, 3, 4), (1, 8, 2, 0), (1, 8, 2, 1025)]:
         assert K.lib().kvq_decode_workspace_bytes(*bad) == -1
 
@@ -589,7 +590,7 @@ def _noalloc(B=1, Hq=8, Hkv=2, n_packed=128, S=4, out=A, od=K.KVQ_OUT_F32, knew=
     (dict(od=5), K.KVQ_ERR_UNSUPPORTED),
     (dict(knew=A), K.KVQ_ERR_NULL),
     (dict(S=0), K.KVQ_ERR_SHAPE),
-    # 8 rows of 4 query heads at 1024 splits need 19.5 MB of records: more than the scratch
+    # 8 rows of 4 query heads at 1024 splits need 17.6 MB of records: more than the scratch
     (dict(B=1, Hq=32, Hkv=8, n_packed=32768, S=1024), K.KVQ_ERR_TOO_LARGE),
 ])
 def test_decode_fused_noalloc_rejects(kw, status):

@@ -87,11 +87,11 @@ def test_fused_small(oracle_mod, case):
     _check(oracle_mod, bits, hybrid, B, Hq, Hkv, n_packed, n_res, S_, seed=sum(case))
 
 
-@pytest.mark.parametrize("S_", [2, 7, 8, 9, 15, 16, 17, 63, 64, 65, 100, 511, 512, 513, 1023,
-                                1024])
+@pytest.mark.parametrize("S_", [2, 7, 8, 9, 31, 32, 33, 63, 64, 65, 100, 511, 512, 513, 993,
+                                1023, 1024])
 def test_fused_split_tree_shapes(oracle_mod, S_):
-    """Split counts that fill the fan-in-8 tree exactly (8, 64, 512), leave a lone child at
-    some level (9, 17, 65, 513) or give one to four levels, over 32K packed tokens (1024
+    """Split counts that fill the fan-in-32 tree exactly (32, 1024), leave a lone child at the
+    first level (33, 65, 513, 993), or give one or two levels, over 32K packed tokens (1024
     tiles) and a full window."""
     _check(oracle_mod, 4, False, 1, 8, 2, 32768, 128, S_, seed=40 + S_)
 

@@ -68,7 +68,7 @@ def test_noalloc_equals_workspace_call_twice_then_smaller(oracle_mod):
 
 
 def test_noalloc_rejects_sizes_beyond_its_scratch():
-    """8 rows of 4 query heads at 1024 splits need 19.5 MB of records: rejected on the host
+    """8 rows of 4 query heads at 1024 splits need 17.6 MB of records: rejected on the host
     with KVQ_ERR_TOO_LARGE before anything is launched."""
     from gpu_common import DEV
     fmt = K.Format(4)
