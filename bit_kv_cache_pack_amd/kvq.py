@@ -446,6 +446,8 @@ def suggest_splits(B: int, Hkv: int, n_tokens: int, cu_count: int = 256) -> int:
         want = (3 * cu_count + rows - 1) // rows
         if tiles < 64 * want:
             want = (2 * cu_count + rows - 1) // rows
+        elif want >= 2:
+            want += 1
     return int(max(1, min(256, min(want, cap))))
 
 

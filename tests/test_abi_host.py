@@ -489,13 +489,18 @@ def test_split_rules_match_the_header(tmp_path):
 
 
 def test_split_rule_on_the_workloads():
-    """One wide workgroup per CU for few rows, else three 4-wave workgroups per CU where
-    splits stay long and two where they would get short; the 8-tile floor for short
-    sequences."""
+    """One wide workgroup per CU for few rows, else three 4-wave workgroups per CU (plus
+    the window's split) where splits stay long and two where they would get short; the
+    8-tile floor for short sequences."""
     import synth_inputs as S
     got = {n: K.suggest_splits(w.B, w.Hkv, w.L) for n, w in S.WORKLOADS.items()}
-    assert got == {"tiny": 4, "llama8b_32k": 32, "batch8_2bit_hybrid": 12,
+    assert got == {"tiny": 4, "llama8b_32k": 32, "batch8_2bit_hybrid": 13,
                    "long_128k_3bit": 32, "mha_b64_append": 1}
+    # three per CU: 64 rows -> 12 packed splits + the window's; 8 rows of 256K tokens ->
+    # 96 + 1; one split (2560 rows) stays one
+    assert K.suggest_splits(8, 8, 32768) == 13
+    assert K.suggest_splits(1, 8, 262144) == 97
+    assert K.suggest_splits(64, 40, 4096) == 1
     # the wide branch: 32 rows on 256 CUs, 8 splits of 128 tiles; one tile more per split
     # leaves it for the per-CU rules (two per CU: 16 splits)
     assert K.suggest_splits(4, 8, 32768) == 8
