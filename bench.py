@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--no-paged", action="store_true")
     ap.add_argument("--no-outer", action="store_true")
     ap.add_argument("--paged-workload", default="paged_ragged_b16")
+    ap.add_argument("--paged-splits", type=int, default=0, help="0 = the library's suggestion")
     ap.add_argument("--copies", type=int, default=0,
                     help="cache copies rotated by the timed loop (0 = enough to exceed 512 MB)")
     ap.add_argument("--no-per-config", action="store_true",
@@ -316,8 +317,9 @@ def paged_bench(args, K, S, dev, stream, sptr, timed):
         (kpool.clone(), vpool.clone(), kr0.clone(), vr0.clone(), state0.clone())
         for _ in range(copies - 1)]
     q = torch.from_numpy(x.q).to(dev)
-    S_ = K.suggest_splits_paged(int(x.n_packed.sum()), int(x.n_packed.max()), Hkv,
-                                torch.cuda.get_device_properties(dev).multi_processor_count)
+    S_ = args.paged_splits or K.suggest_splits_paged(
+        int(x.n_packed.sum()), int(x.n_packed.max()), Hkv,
+        torch.cuda.get_device_properties(dev).multi_processor_count)
     po = torch.empty((B, Hq, S_, 128), dtype=torch.float32, device=dev)
     pl = torch.empty((B, Hq, S_), dtype=torch.float32, device=dev)
     out = torch.empty((B, Hq, 128), dtype=torch.float16, device=dev)
