@@ -810,6 +810,10 @@ __global__ __launch_bounds__(64 * W) __attribute__((amdgpu_waves_per_eu(OUTER ? 
                 // the transposed order of 4-bit K codes in LDS (issue_tile_at)
                 *reinterpret_cast<uint32_t *>(cb + (t >> 4) * 1024 + grp * 256 + (t & 15) * 16 +
                                               jq * 4) = packed;
+            } else if (!is_v && BITS == 2) {
+                // the transposed order of 2-bit K codes in LDS (issue_tile_at)
+                *reinterpret_cast<uint16_t *>(cb + (t >> 4) * 512 + (grp >> 1) * 256 + (t & 15) * 16 +
+                                              (grp & 1) * 8 + jq * 2) = (uint16_t)packed;
             } else {
                 uint8_t *c = cb + t * G::TOKB + grp * (4 * BITS) + jq * BITS;
                 if (BITS == 4) {

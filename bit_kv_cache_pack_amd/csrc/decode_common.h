@@ -122,12 +122,15 @@ __device__ __forceinline__ void issue_tile_at(__amdgpu_buffer_rsrc_t rk, __amdgp
             dma_nt(rv, slot + G::CB + 1024, c0 + 1024 + lane * 16);
         }
     } else {
-        // 4-bit K codes: each 1 KB request (16 tokens x 64 B) lands transposed in LDS, the
-        // 16-byte piece of group r of token n at position 16 r + n (KGroup<4>::load), so
-        // that the 128-bit reads of one group for 16 tokens are consecutive in LDS (no bank
-        // conflict); the request still reads the same whole 1 KB
+        // K codes land with their 16-byte pieces transposed in LDS, so that the reads of
+        // one group for 16 tokens hit every bank once (no conflict): at 4 bits each 1 KB
+        // request (16 tokens x 64 B) puts the piece of group r of token n at position
+        // 16 r + n (KGroup<4>::load); at 2 bits each 512 B half (16 tokens x 32 B) puts
+        // piece j (groups 2j, 2j+1) of token n at position 16 j + n (KGroup<2>::load).
+        // A request still reads the same whole 1 KB.
         const uint32_t koff = BITS == 4 ? (uint32_t)(64 * (lane & 15) + 16 * (lane >> 4))
-                                        : (uint32_t)lane * 16u;
+                                        : (uint32_t)(512 * (lane >> 5) + 32 * (lane & 15) +
+                                                     16 * ((lane >> 4) & 1));
 #pragma unroll
         for (int k = 0; k < G::CB / 1024; ++k) {
             dma_nt(rk, slot + 1024 * k, c0 + 1024 * k + koff);
@@ -209,9 +212,12 @@ struct KGroup<4> {
 template <>
 struct KGroup<2> {
     u32x2 w;
+    // group r of token t: half r % 2 of piece 16 (r / 2) + t % 16 of the tokens' 512 B half
+    // (the transposed order issue_tile_at writes)
     __device__ __forceinline__ void load(const uint8_t *slot, int t, int r)
     {
-        w = *reinterpret_cast<const u32x2 *>(slot + t * 32 + r * 8);
+        w = *reinterpret_cast<const u32x2 *>(slot + (t >> 4) * 512 + (r >> 1) * 256 + (t & 15) * 16 +
+                                             (r & 1) * 8);
     }
     __device__ __forceinline__ half8_t octet(int o, const Magic &M) const
     {
