@@ -242,7 +242,7 @@ def _random_cases(n, seed=2024):
     return out
 
 
-@pytest.mark.parametrize("case", _random_cases(24), ids=lambda c: f"r{c[0]}")
+@pytest.mark.parametrize("case", _random_cases(64), ids=lambda c: f"r{c[0]}")
 def test_decode_random_shapes(oracle_mod, case):
     """Seeded random shapes (bits, hybrid, batch, GQA 1-16, packed length, window fill and
     capacity, split count): output and partials against the oracle; where the window is not

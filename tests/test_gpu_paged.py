@@ -505,6 +505,8 @@ def test_serving_run_with_key_normalization(oracle_mod):
     (3, True, 16, 2, 8, 1, 20, 4, "head_major", False),    # gq 8: two launches inside the call
     (4, False, 8, 2, 16, 4, 12, 3, "block_major", True),   # with key-channel factors
     (2, True, 16, 2, 8, 0, 12, 2, "head_major", True),     # the same through two launches
+    (2, False, 8, 2, 16, 4, 40, 5, "block_major", False),  # 2-bit asym, gq 4 (transposed K in LDS)
+    (3, False, 8, 2, 16, 4, 40, 7, "block_major", False),  # 3-bit, gq 4
 ])
 def test_paged_append_equals_update_then_decode(oracle_mod, bits, hybrid, Hq, Hkv, cap, n_sink,
                                                 steps, S_, layout, knorm):
