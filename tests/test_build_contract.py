@@ -98,3 +98,62 @@ def test_no_inline_asm_vgpr_writes():
             if tmpl.strip() and re.search(r'"[=+&]*v"', outputs):
                 bad.append(f"{name}: {tmpl.strip()}")
     assert not bad, bad
+
+
+# ---- direct-to-LDS loads: the LDS base (M0) must be one wave-uniform value -------------
+# A direct-to-LDS buffer load writes lane i's bytes at M0 + size * i. When the compiler
+# merges two such calls with different LDS pointers (one under a lane condition, one not)
+# into one call on a per-lane pointer, it sets M0 from v_readfirstlane of that pointer:
+# every lane then writes relative to lane 0's base, silently overwriting the wrong part of
+# LDS. This was seen with a reordered 3-bit tile load; the check keeps it from coming back.
+
+_WRITES = re.compile(r"^\s*(?:s_|v_readfirstlane)\S*\s+(s\d+|s\[(\d+):(\d+)\])\s*,")
+
+
+def _sgpr_range(tok, lo, hi):
+    if lo is not None:
+        return range(int(lo), int(hi) + 1)
+    return range(int(tok[1:]), int(tok[1:]) + 1)
+
+
+def _m0_from_readfirstlane(asm_text):
+    bad = []
+    lines = asm_text.splitlines()
+    for k, line in enumerate(lines):
+        m = re.match(r"^\s*s_\w+\s+m0\s*,\s*(s\d+)", line)
+        if not m:
+            continue
+        reg = int(m.group(1)[1:])
+        for j in range(k - 1, max(k - 400, -1), -1):
+            prev = lines[j]
+            if re.match(r"^\S.*:\s*(;.*)?$", prev) and not prev.startswith(("\t", " ")):
+                if re.match(r"^[._A-Za-z0-9]+:", prev) and not prev.startswith(".LBB"):
+                    break                                     # start of another function
+            w = _WRITES.match(prev)
+            if w and reg in _sgpr_range(w.group(1), w.group(2), w.group(3)):
+                if prev.strip().startswith("v_readfirstlane"):
+                    bad.append((k, prev.strip(), line.strip()))
+                break
+    return bad
+
+
+def test_scanner_flags_m0_from_readfirstlane():
+    asm = ("_Z1kv:\n\tv_readfirstlane_b32 s10, v4\n\ts_mov_b32 s42, s38\n"
+           "\ts_mov_b32 m0, s10\n\tbuffer_load_dwordx4 v2, s[40:43], 0 offen lds\n"
+           "\ts_add_i32 s11, s33, 0x400\n\ts_mov_b32 m0, s11\n")
+    bad = _m0_from_readfirstlane(asm)
+    assert len(bad) == 1 and "v_readfirstlane" in bad[0][1]
+
+
+@pytest.mark.parametrize("src", ["decode_attn.hip", "decode_valu.hip"])
+def test_lds_dma_base_is_uniform(tmp_path, src):
+    """No M0 in the kernels that load tiles straight into LDS comes from v_readfirstlane."""
+    hipcc = B.hipcc()
+    if not (os.path.exists(hipcc) or shutil.which(hipcc)):
+        pytest.skip("hipcc not available")
+    asm = tmp_path / (src + ".s")
+    r = subprocess.run([hipcc, *B.compile_flags(), "--cuda-device-only", "-S", "-o", str(asm),
+                        os.path.join(B.CSRC, src)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-2000:]
+    bad = _m0_from_readfirstlane(asm.read_text())
+    assert not bad, bad[:3]
